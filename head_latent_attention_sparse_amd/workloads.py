@@ -1,0 +1,204 @@
+"""Seeded synthetic inputs for the five sparse-MLA workloads.
+
+This module only draws random numbers and lays them out (CSR lists, block
+tables, slot mappings).  It holds none of the method's arithmetic, so the
+HIP path and the CPU oracle can both take their inputs from it.
+
+Every tensor is drawn on the CPU from ``torch.Generator().manual_seed(seed)``
+in the order written below; float values are drawn as float32 and rounded to
+bf16 (round to nearest even).  "N(0, s)" means standard deviation s.
+
+The shapes follow the workloads the pages serve: DeepSeek-V3.2 / Kimi-K3
+sparse prefill over the fp8_ds_mla cache with at most 16 heads per rank
+(flydsl_sparse_mla page, module docstring), paged decode over a block table
+(fused_mla_key_concat_kv_cache page; kimi_k3 nvidia mla page), 12 heads per
+rank at TP8 (mono/attention/mla page, module docstring), a 576-wide absorbed
+query [ql_nope | q_pe] and a 192^-0.5 softmax scale (qk_nope 128 + qk_rope 64;
+kimi_k3 nvidia mla page, ``__init__``).
+"""
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import torch
+
+SEED_BASE = 20261202
+QK_HEAD_DIM = 192  # qk_nope_head_dim 128 + qk_rope_head_dim 64
+SOFTMAX_SCALE = QK_HEAD_DIM**-0.5
+D_QK = 576
+LATENT = 512
+ROPE = 64
+
+
+@dataclass
+class InsertBatch:
+    kv_c: torch.Tensor  # bf16 [n, 512]
+    k_pe: torch.Tensor  # bf16 [n, 64]
+    slots: torch.Tensor  # int64 [n], -1 = skip
+
+
+@dataclass
+class Workload:
+    name: str
+    num_records: int
+    q: torch.Tensor  # bf16 [T, H, 576]
+    indptr: torch.Tensor  # int32 [T + 1]
+    indices: torch.Tensor  # int32 [nnz]
+    softmax_scale: float
+    has_invalid: bool
+    return_lse: bool
+    # Insert batches that build the pool from zero bytes, applied in order.
+    setup_inserts: List[InsertBatch] = field(default_factory=list)
+    # Insert batches that belong to the timed step (before the forward).
+    step_inserts: List[InsertBatch] = field(default_factory=list)
+    block_size: Optional[int] = None  # pool viewed as [nb, block_size, 656]
+
+    @property
+    def num_tokens(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_heads(self) -> int:
+        return self.q.shape[1]
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indices.numel())
+
+    def nnz_valid(self) -> int:
+        ok = (self.indices >= 0) & (self.indices < self.num_records)
+        return int(ok.sum())
+
+
+def _bf16(g: torch.Generator, shape, std: float = 1.0) -> torch.Tensor:
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
+def _csr(rows: List[torch.Tensor]) -> Tuple[torch.Tensor, torch.Tensor]:
+    lengths = torch.tensor([0] + [int(r.numel()) for r in rows], dtype=torch.int64)
+    indptr = torch.cumsum(lengths, 0).to(torch.int32)
+    if rows:
+        indices = torch.cat([r.to(torch.int32) for r in rows])
+    else:
+        indices = torch.zeros(0, dtype=torch.int32)
+    return indptr, indices
+
+
+def _pool_fill(g: torch.Generator, n: int, latent_std: float = 1.0) -> InsertBatch:
+    kv_c = _bf16(g, (n, LATENT), latent_std)
+    k_pe = _bf16(g, (n, ROPE))
+    return InsertBatch(kv_c, k_pe, torch.arange(n, dtype=torch.int64))
+
+
+def tiny(tokens: int = 4, heads: int = 16, records: int = 2048, per_row: int = 128) -> Workload:
+    """Config 1: 4 rows x 128 distinct random slots over a 2048-record cache."""
+    g = torch.Generator().manual_seed(SEED_BASE + 1)
+    fill = _pool_fill(g, records)
+    q = _bf16(g, (tokens, heads, D_QK))
+    rows = [torch.randperm(records, generator=g)[:per_row] for _ in range(tokens)]
+    indptr, indices = _csr(rows)
+    return Workload("tiny", records, q, indptr, indices, SOFTMAX_SCALE,
+                    has_invalid=False, return_lse=True, setup_inserts=[fill])
+
+
+def paged_decode(batch: int = 64, heads: int = 16, len_lo: int = 1024, len_hi: int = 8192,
+                 block_size: int = 64) -> Workload:
+    """Config 2: one query row per request over a paged pool and a random block table.
+
+    Context lengths are uniform on [len_lo, len_hi] (inclusive).  The pool holds
+    exactly the blocks the requests need; a random permutation of the blocks is
+    dealt to the requests in order, and position j of request b reads slot
+    ``table[b][j // block_size] * block_size + j % block_size``.
+    """
+    g = torch.Generator().manual_seed(SEED_BASE + 2)
+    lengths = torch.randint(len_lo, len_hi + 1, (batch,), generator=g)
+    blocks_per = [(int(n) + block_size - 1) // block_size for n in lengths]
+    num_blocks = sum(blocks_per)
+    fill = _pool_fill(g, num_blocks * block_size)
+    q = _bf16(g, (batch, heads, D_QK))
+    perm = torch.randperm(num_blocks, generator=g)
+    rows, start = [], 0
+    for n, nb in zip(lengths.tolist(), blocks_per):
+        table = perm[start : start + nb]
+        start += nb
+        pos = torch.arange(n, dtype=torch.int64)
+        rows.append(table[pos // block_size] * block_size + pos % block_size)
+    indptr, indices = _csr(rows)
+    return Workload("paged_decode", num_blocks * block_size, q, indptr, indices, SOFTMAX_SCALE,
+                    has_invalid=False, return_lse=True, setup_inserts=[fill],
+                    block_size=block_size)
+
+
+def sparse_prefill(tokens: int = 4096, heads: int = 16, records: int = 131072,
+                   per_row: int = 2048, p_invalid: float = 0.10,
+                   frac_empty: float = 0.01) -> Workload:
+    """Config 3: top-k style sparse prefill.
+
+    Each row lists ``per_row`` distinct uniform slots; then round(frac_empty * T)
+    random rows are set entirely to -1, and every other entry is set to -1
+    independently with probability ``p_invalid``.
+    """
+    g = torch.Generator().manual_seed(SEED_BASE + 3)
+    fill = _pool_fill(g, records)
+    q = _bf16(g, (tokens, heads, D_QK))
+    idx = torch.stack([torch.randperm(records, generator=g)[:per_row] for _ in range(tokens)])
+    n_empty = int(round(frac_empty * tokens))
+    empty_rows = torch.randperm(tokens, generator=g)[:n_empty]
+    drop = torch.rand((tokens, per_row), generator=g) < p_invalid
+    idx[drop] = -1
+    idx[empty_rows] = -1
+    indptr = torch.arange(0, tokens * per_row + 1, per_row, dtype=torch.int64).to(torch.int32)
+    return Workload("sparse_prefill", records, q, indptr, idx.reshape(-1).to(torch.int32),
+                    SOFTMAX_SCALE, has_invalid=True, return_lse=True, setup_inserts=[fill])
+
+
+def long_context(tokens: int = 8, heads: int = 16, records: int = 131072,
+                 latent_std: float = 2.0) -> Workload:
+    """Config 4: few rows, each a random permutation of the whole cache."""
+    g = torch.Generator().manual_seed(SEED_BASE + 4)
+    fill = _pool_fill(g, records, latent_std)
+    q = _bf16(g, (tokens, heads, D_QK))
+    rows = [torch.randperm(records, generator=g) for _ in range(tokens)]
+    indptr, indices = _csr(rows)
+    return Workload("long_context", records, q, indptr, indices, SOFTMAX_SCALE,
+                    has_invalid=False, return_lse=True, setup_inserts=[fill])
+
+
+def insert_attend(pool: int = 65536, new_tokens: int = 4096, p_skip: float = 0.05,
+                  tokens: int = 1024, heads: int = 12, per_row: int = 1024) -> Workload:
+    """Config 5: insert new tokens into a filled pool, then attend over it.
+
+    The pool is first filled at every slot; the step inserts ``new_tokens``
+    tokens at distinct random slots, each slot set to -1 (skipped) with
+    probability ``p_skip``, then runs the forward with ``per_row`` distinct
+    random slots per row.
+    """
+    g = torch.Generator().manual_seed(SEED_BASE + 5)
+    fill = _pool_fill(g, pool)
+    kv_c = _bf16(g, (new_tokens, LATENT))
+    k_pe = _bf16(g, (new_tokens, ROPE))
+    slots = torch.randperm(pool, generator=g)[:new_tokens].to(torch.int64)
+    slots[torch.rand(new_tokens, generator=g) < p_skip] = -1
+    q = _bf16(g, (tokens, heads, D_QK))
+    rows = [torch.randperm(pool, generator=g)[:per_row] for _ in range(tokens)]
+    indptr, indices = _csr(rows)
+    return Workload("insert_attend", pool, q, indptr, indices, SOFTMAX_SCALE,
+                    has_invalid=False, return_lse=True, setup_inserts=[fill],
+                    step_inserts=[InsertBatch(kv_c, k_pe, slots)])
+
+
+CONFIGS = {
+    1: tiny,
+    2: paged_decode,
+    3: sparse_prefill,
+    4: long_context,
+    5: insert_attend,
+}
+
+
+def bf16_bits(t: torch.Tensor):
+    """A bf16 tensor's bit patterns as a numpy uint16 array (CPU copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")

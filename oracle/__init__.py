@@ -1,0 +1,38 @@
+"""CPU oracle for the sparse absorbed-MLA forward and the fp8_ds_mla cache insert.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, links or
+calls this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` do.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers), and it never consumes a
+value produced by the HIP path.
+
+Everything here is plain numpy in float64 (float32 only where the pages fix
+the arithmetic of the insert writer), written from the definitions on the
+vLLM API pages:
+
+* ``vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla`` (module docstring, and
+  the ``flydsl_sparse_mla_fp8ds_fwd`` / ``..._supported`` docstrings): the
+  656-byte record, the CSR slot lists, masking of negative ids, the
+  empty-row convention and the natural-log LSE;
+* ``vllm.models.kimi_k3.nvidia.ops.fused_mla_key_concat_kv_cache``
+  (``fused_mla_key_concat_ds_mla_insert`` docstring): the self-scaling
+  record writer with per-128-tile dynamic fp8 scales;
+* ``vllm.models.kimi_k3.nvidia.mla`` (``_compute_prefill_context`` and
+  ``merge_attn_states`` call): combining attention partials by their LSEs.
+
+Modules:
+  e4m3       OCP float8 E4M3 ("fn") decode table and saturating RNE encoder.
+  records    656-byte record encode (the insert writer) and decode.
+  attention  Sparse attention forward over records, and the LSE merge.
+
+Parity pins for every function live in ``tests/test_oracle_*.py``.
+"""
+
+from .e4m3 import E4M3_MAX, decode_table, e4m3_decode, e4m3_encode  # noqa: F401
+from .records import (  # noqa: F401
+    RECORD_BYTES,
+    decode_records,
+    encode_records,
+    insert_records,
+)
+from .attention import merge_partials, sparse_fwd  # noqa: F401
