@@ -55,24 +55,22 @@ def e4m3_encode(x):
     x = np.asarray(x, dtype=np.float64)
     negative = np.signbit(x)
     a = np.minimum(np.abs(x), E4M3_MAX)  # saturate; |x| only from here on
-    codes = np.zeros(x.shape, dtype=np.int64)
 
     # Subnormal range |x| < 2^-6: the code is the integer m with value
     # m * 2^-9; rounding |x| * 2^9 to the nearest even integer is exact in
     # float64 (scaling by a power of two) and may give m = 8, which is the
     # smallest normal 0x08 = 2^-6, so the two ranges join without a seam.
-    sub = a < 2.0**-6
-    codes[sub] = np.rint(a[sub] * 2.0**9).astype(np.int64)
+    sub_code = np.rint(a * 2.0**9)
 
     # Normal range: a = 2^e * (1 + f), keep 3 fraction bits with RNE.  A
     # carry out of the fraction (mantissa 8) bumps the exponent, which the
     # integer sum below does by itself.
-    nrm = ~sub & ~np.isnan(a)
-    frac, exp2 = np.frexp(a[nrm])  # a = frac * 2^exp2, frac in [0.5, 1)
-    e = exp2 - 1  # unbiased exponent of a
-    mant = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)  # 0..8, exact
-    codes[nrm] = ((e + 7) << 3) + mant
+    frac, exp2 = np.frexp(a)  # a = frac * 2^exp2, frac in [0.5, 1)
+    e = exp2.astype(np.int64) - 1  # unbiased exponent of a
+    mant = np.rint((2.0 * frac - 1.0) * 8.0)  # 0..8, exact
+    nrm_code = ((e + 7) << 3) + mant.astype(np.int64)
 
-    codes[np.isnan(a)] = 0x7F
+    codes = np.where(a < 2.0**-6, sub_code.astype(np.int64), nrm_code)
+    codes = np.where(np.isnan(a), 0x7F, codes)
     codes = codes | np.where(negative, 0x80, 0)
     return codes.astype(np.uint8)
