@@ -1,0 +1,235 @@
+"""Benchmark of the sparse MLA forward on MI355X (one GPU).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+                [--no-cpu-baseline] [--copy-calibration]
+
+A step is one pass of the hot path over the workload: for the sparse top-k
+prefill workload (the default) that is one mla_sparse_fwd call over all
+4096 rows; for the insert + attend workload it is the insert of the new
+tokens followed by the forward.  Inputs are synthetic, seeded, and resident
+in HBM before timing starts.  Prints ONE JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FWD_KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_sparse_amd", "csrc", "sparse_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_fwd_sparse_prefill_traffic.json")
+
+WORKLOAD_NAMES = {
+    1: "tiny: T=4 rows, H=16, 128 distinct slots/row over 2048 records",
+    2: "paged decode: B=64 rows, H=16, context U[1024,8192], block 64",
+    3: "sparse top-k prefill: T=4096 rows, H=16, 2048 slots/row over 131072 records, 10% -1, 1% empty rows",
+    4: "long context: T=8 rows, H=16, 131072 slots/row (split-KV + LSE merge)",
+    5: "insert + attend: insert 4096 tokens (5% skipped) into 65536 records, then T=1024, H=12, 1024 slots/row",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    with open(FWD_KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(rows would shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating workload {args.config}")
+    w = workloads.CONFIGS[args.config]()
+    t_count, heads = w.num_tokens, w.num_heads
+    nnz, nnz_valid = w.nnz, w.nnz_valid()
+
+    # ---- inputs resident in HBM
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=dev)
+    view = pool.view(-1, w.block_size, 656) if w.block_size else pool
+    for b in w.setup_inserts:
+        mla.cache_insert(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev), view)
+    step_inserts = [(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev)) for b in w.step_inserts]
+    q = w.q.to(dev)
+    indptr, indices = w.indptr.to(dev), w.indices.to(dev)
+    out = torch.empty((t_count, heads, 512), dtype=torch.bfloat16, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    splits = mla.num_splits(t_count, nnz, cus)
+    ws_bytes = mla.lib().mla_sparse_fwd_workspace_size(t_count, heads, nnz, 0, 0)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step():
+        for kv_c, k_pe, slots in step_inserts:
+            mla.cache_insert(kv_c, k_pe, slots, view)
+        return mla.sparse_fwd(q, view, indptr, indices, w.softmax_scale, has_invalid=w.has_invalid,
+                              out=out, return_lse=w.return_lse, workspace=workspace)
+
+    log("inputs resident; warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; a HIP event pair around each step on the
+    # stream the kernels are launched on (torch's current stream).
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    dev_ms = float(np.mean(step_ms))
+
+    _, lse = step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+
+    pairs_h = nnz * heads
+    value = pairs_h / (ms_per_step * 1e-3)
+    gathered = nnz_valid * 656.0
+    flops = nnz_valid * heads * 2.0 * (576 + 512)
+    achieved_gbps = gathered / (dev_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and args.config == 3:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256_16") == source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": "sparse MLA fwd: (row,key) pairs/s x H and achieved HBM GB/s on 656B records",
+        "value": value,
+        "unit": "pairs*H/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "rows": t_count,
+            "heads": heads,
+            "records": w.num_records,
+            "csr_entries": nnz,
+            "valid_entries": nnz_valid,
+            "splits": splits,
+            "parallelism": "single GPU",
+        },
+        "gathered_record_GBps": gathered / (ms_per_step * 1e-3) / 1e9,
+        "valid_pairs_H_per_s": nnz_valid * heads / (ms_per_step * 1e-3),
+        "device_ms_per_step": dev_ms,
+        "mfma_tflops": flops / (dev_ms * 1e-3) / 1e12,
+        "mfma_frac": flops / (dev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": gathered,
+        },
+    }
+
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {dev_ms:.3f} ms)")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, target_seconds):
+    """The fp64 oracle on a bounded sample of the same workload's rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import encode_records, sparse_fwd
+    from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+    indptr, indices = w.indptr.numpy().astype(np.int64), w.indices.numpy().astype(np.int64)
+    batches = w.setup_inserts + w.step_inserts
+    with threadpool_limits(limits=1):
+        # records of the workload, by the oracle's own writer (untimed setup)
+        pool = np.zeros((w.num_records, 656), dtype=np.uint8)
+        for b in batches:
+            slots = b.slots.numpy()
+            keep = (slots >= 0) & (slots < w.num_records)
+            kv, pe = bf16_bits(b.kv_c)[keep], bf16_bits(b.k_pe)[keep]
+            recs = [encode_records(kv[i:i + 8192], pe[i:i + 8192]) for i in range(0, kv.shape[0], 8192)]
+            pool[slots[keep]] = np.concatenate(recs)
+        q_bits = bf16_bits(w.q)
+        log("oracle records written; timing the oracle forward")
+        rows, pairs, elapsed, t = [], 0, 0.0, 0
+        # rows in order until the target CPU time is reached
+        while t < w.num_tokens and elapsed < target_seconds:
+            batch = list(range(t, min(t + 8, w.num_tokens)))
+            t0 = time.perf_counter()
+            sparse_fwd(q_bits, pool, indptr, indices, w.softmax_scale, rows=batch)
+            elapsed += time.perf_counter() - t0
+            pairs += int(indptr[batch[-1] + 1] - indptr[batch[0]])
+            rows.extend(batch)
+            t += len(batch)
+    return {
+        "value": pairs * w.num_heads / elapsed,
+        "unit": "pairs*H/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"rows 0..{len(rows) - 1} of {w.num_tokens} ({pairs} CSR entries), fp64 numpy oracle, "
+                  f"one thread, {elapsed:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

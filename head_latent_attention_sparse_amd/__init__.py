@@ -1,0 +1,21 @@
+"""Sparse absorbed-MLA forward over an fp8_ds_mla latent cache, for MI355X (gfx950).
+
+The computation lives in libmla.so (hand-written HIP kernels behind the C
+ABI of include/mla.h); this package is its thin Python binding.
+"""
+
+from .ops import (  # noqa: F401
+    FLAG_HAS_INVALID,
+    FLAG_INDEX_I64,
+    FLAG_RETURN_LSE,
+    KV_LORA_RANK,
+    MAX_HEADS,
+    MAX_SPLITS,
+    QK_ROPE_HEAD_DIM,
+    RECORD_BYTES,
+    MlaError,
+    cache_insert,
+    lib,
+    num_splits,
+    sparse_fwd,
+)

@@ -1,0 +1,282 @@
+// C ABI of the sparse MLA library: argument validation (host metadata only),
+// split-KV planning, the library-owned workspace, and kernel launches.
+//
+// The validation restates the limits flydsl_sparse_mla_fp8ds_supported
+// states on the flydsl_sparse_mla page (head count, 576-wide bf16 rows with
+// even strides and a 4-byte aligned base, 16-byte aligned 656-byte records
+// at their natural pitch, int32/int64 CSR arrays, fewer than 2^29 indices),
+// in C terms: every rejection happens before anything is queued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+mla_status_t fail(mla_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Compute units of the current device (cached per device).
+int device_cus(int device) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0) return 0;
+  if ((size_t)device >= cache.size()) cache.resize(device + 1, 0);
+  if (cache[device] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+    cache[device] = cus;
+  }
+  return cache[device];
+}
+
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+
+// Grow device `device`'s library-owned workspace to >= bytes; returns it.
+mla_status_t workspace_get(int device, size_t bytes, void **out) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if ((size_t)device >= g_ws.size()) g_ws.resize(device + 1);
+  Workspace &w = g_ws[device];
+  if (w.bytes < bytes) {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed");
+    if (prev != device && hipSetDevice(device) != hipSuccess) return fail(MLA_ERR_HIP, "hipSetDevice(%d) failed", device);
+    if (w.ptr) {
+      // hipFree waits for work that may still use the old buffer.
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t want = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+    hipError_t e = hipMalloc(&w.ptr, want);
+    if (prev != device) (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      (void)hipGetLastError();
+      return fail(MLA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated on device %d: %s", want,
+                  device, hipGetErrorString(e));
+    }
+    w.bytes = want;
+  }
+  *out = w.ptr;
+  return MLA_OK;
+}
+
+constexpr uint32_t kKnownFlags =
+    MLA_FLAG_HAS_INVALID | MLA_FLAG_RETURN_LSE | MLA_FLAG_INDEX_I64 | MLA_FLAG_SPLITS_MASK;
+
+// Entries per split below which splitting a row further does not pay: eight
+// 64-key tiles.
+constexpr int64_t kMinEntriesPerSplit = 512;
+
+int32_t plan_splits(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags) {
+  const uint32_t forced = (flags & MLA_FLAG_SPLITS_MASK) >> 16;
+  if (forced) return forced > MLA_MAX_SPLITS ? MLA_MAX_SPLITS : (int32_t)forced;
+  if (tokens <= 0 || cus <= 0) return 1;
+  // Aim for two resident workgroups per compute unit over the whole launch,
+  // but never split a row's average share below kMinEntriesPerSplit.
+  const int64_t target = 2 * (int64_t)cus;
+  if (tokens >= target) return 1;
+  int64_t s = (target + tokens - 1) / tokens;
+  const int64_t by_len = (nnz / tokens) / kMinEntriesPerSplit;
+  if (s > by_len) s = by_len;
+  if (s < 1) s = 1;
+  if (s > MLA_MAX_SPLITS) s = MLA_MAX_SPLITS;
+  return (int32_t)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_last_error(void) { return g_error; }
+
+const char *mla_status_string(mla_status_t st) {
+  switch (st) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_OUT_OF_MEMORY: return "MLA_ERR_OUT_OF_MEMORY";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int32_t mla_sparse_fwd_num_splits(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags) {
+  if (num_tokens < 0 || num_indices < 0 || num_cus < 0 || (flags & ~kKnownFlags)) return 0;
+  return plan_splits(num_tokens, num_indices, num_cus, flags);
+}
+
+size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_indices, uint32_t flags,
+                                     int device) {
+  if (num_tokens < 0 || num_indices < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS || (flags & ~kKnownFlags)) {
+    fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd_workspace_size: invalid arguments");
+    return (size_t)-1;
+  }
+  const uint32_t forced = (flags & MLA_FLAG_SPLITS_MASK) >> 16;
+  int cus = 0;
+  if (!forced) {
+    cus = device_cus(device);
+    if (cus <= 0) {
+      fail(MLA_ERR_HIP, "mla_sparse_fwd_workspace_size: cannot query device %d", device);
+      return (size_t)-1;
+    }
+  }
+  return mla::split_workspace_bytes(num_tokens, num_heads, plan_splits(num_tokens, num_indices, cus, flags));
+}
+
+mla_status_t mla_workspace_reserve(int device, size_t bytes) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_workspace_reserve: no device %d", device);
+  void *p = nullptr;
+  return workspace_get(device, bytes, &p);
+}
+
+mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                            int64_t q_stride_head, const void *kv_records, int64_t num_records, int64_t record_stride,
+                            const void *kv_indptr, const void *kv_indices, int64_t num_indices, float softmax_scale,
+                            uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head, float *lse,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  if (flags & ~kKnownFlags) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: unknown flag bits 0x%x", flags & ~kKnownFlags);
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens > INT32_MAX - 1) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_tokens %lld too large", (long long)num_tokens);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_heads %d outside 1..%d", num_heads, MLA_MAX_HEADS);
+  if (q_stride_token < 0 || q_stride_head < 0 || out_stride_token < 0 || out_stride_head < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: negative stride");
+  if ((q_stride_token | q_stride_head) & 1)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q strides must be even (got %lld, %lld)", (long long)q_stride_token,
+                (long long)q_stride_head);
+  if ((out_stride_token | out_stride_head) & 1)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out strides must be even (got %lld, %lld)",
+                (long long)out_stride_token, (long long)out_stride_head);
+  if (record_stride != MLA_RECORD_BYTES)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
+                MLA_RECORD_BYTES);
+  if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_records %lld < 0", (long long)num_records);
+  if (num_records > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_records %lld >= 2^31", (long long)num_records);
+  if (num_indices < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_indices %lld < 0", (long long)num_indices);
+  if (num_indices >= MLA_MAX_INDICES)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_indices %lld >= 2^29", (long long)num_indices);
+  const bool i64 = (flags & MLA_FLAG_INDEX_I64) != 0;
+  const bool want_lse = (flags & MLA_FLAG_RETURN_LSE) != 0;
+  const uintptr_t idx_align = i64 ? 8 : 4;
+  if (!aligned(q, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q base not 4-byte aligned");
+  if (!aligned(out, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out base not 4-byte aligned");
+  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: kv_records base not 16-byte aligned");
+  if (!aligned(kv_indptr, idx_align) || !aligned(kv_indices, idx_align))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: index arrays not aligned to their element size");
+  if (want_lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: lse not 4-byte aligned");
+  if (num_tokens == 0) return MLA_OK;
+  if (!q || !out || !kv_indptr) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL q, out or kv_indptr");
+  if (want_lse && !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: MLA_FLAG_RETURN_LSE with lse == NULL");
+  if (num_indices > 0 && !kv_indices) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_indices");
+  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_records");
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: hipGetDevice failed");
+  const int32_t forced = (int32_t)((flags & MLA_FLAG_SPLITS_MASK) >> 16);
+  const int cus = forced ? 0 : device_cus(device);
+  if (!forced && cus <= 0) return fail(MLA_ERR_HIP, "mla_sparse_fwd: cannot query device %d", device);
+  const int32_t splits = plan_splits(num_tokens, num_indices, cus, flags);
+  if ((int64_t)num_tokens * splits > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: %lld rows x %d splits exceeds the grid", (long long)num_tokens, splits);
+
+  mla::FwdArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.q_stride_token = q_stride_token;
+  a.q_stride_head = q_stride_head;
+  a.records = static_cast<const uint8_t *>(kv_records);
+  a.num_records = num_records;
+  a.indptr = kv_indptr;
+  a.indices = num_indices > 0 ? kv_indices : kv_indptr;  // never read when empty
+  a.num_indices = num_indices;
+  a.index_i64 = i64;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.num_tokens = (int32_t)num_tokens;
+  a.num_heads = num_heads;
+  a.out = static_cast<uint16_t *>(out);
+  a.out_stride_token = out_stride_token;
+  a.out_stride_head = out_stride_head;
+  a.lse = want_lse ? lse : nullptr;
+  a.splits = splits;
+  a.ws_out = nullptr;
+  a.ws_lse = nullptr;
+  if (splits > 1) {
+    const size_t need = mla::split_workspace_bytes(num_tokens, num_heads, splits);
+    void *ws = workspace;
+    if (ws) {
+      if (workspace_bytes < need)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+      if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace not 256-byte aligned");
+    } else {
+      mla_status_t st = workspace_get(device, need, &ws);
+      if (st != MLA_OK) return st;
+    }
+    a.ws_out = static_cast<float *>(ws);
+    a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                         mla::split_workspace_lse_offset(num_tokens, num_heads, splits));
+  }
+  hipError_t e = mla::launch_sparse_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_cache_insert(const void *kv_c, int64_t kv_c_stride_token, const void *k_pe, int64_t k_pe_stride_token,
+                              const int64_t *slot_mapping, int64_t num_tokens, void *kv_records, int64_t num_records,
+                              int64_t record_stride, void *stream) {
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: num_tokens %lld < 0", (long long)num_tokens);
+  if (kv_c_stride_token < 0 || k_pe_stride_token < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: negative stride");
+  if ((kv_c_stride_token | k_pe_stride_token) & 1)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: kv_c / k_pe row strides must be even");
+  if (record_stride != MLA_RECORD_BYTES)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
+                MLA_RECORD_BYTES);
+  if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: num_records %lld < 0", (long long)num_records);
+  if (!aligned(kv_c, 4) || !aligned(k_pe, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: kv_c / k_pe not 4-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: slot_mapping not 8-byte aligned");
+  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: kv_records base not 16-byte aligned");
+  if (num_tokens == 0) return MLA_OK;
+  if (!kv_c || !k_pe || !slot_mapping) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: NULL kv_c, k_pe or slot_mapping");
+  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: NULL kv_records");
+  if (num_tokens > ((int64_t)INT32_MAX) * 4) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: too many tokens");
+  mla::InsertArgs a;
+  a.kv_c = static_cast<const uint16_t *>(kv_c);
+  a.kv_c_stride = kv_c_stride_token;
+  a.k_pe = static_cast<const uint16_t *>(k_pe);
+  a.k_pe_stride = k_pe_stride_token;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.records = static_cast<uint8_t *>(kv_records);
+  a.num_records = num_records;
+  hipError_t e = mla::launch_cache_insert(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_cache_insert: launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,402 @@
+// Sparse absorbed-MLA forward over fp8_ds_mla records, for gfx950.
+//
+// What it computes is the sparse_mla_fwd semantics of
+// flydsl_sparse_mla_fp8ds_fwd (vLLM API page
+// vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla, function docstring): for
+// each query row t and head h, softmax(scale * q . k) . v over the row's CSR
+// slot list, keys k = [latent | rope] (576), values v = latent (512),
+// negative slots masked, an empty row giving out 0 and lse -inf.
+//
+// Design (one workgroup of 4 waves per (row, split), 64-key tiles):
+//  * the 64 records of a tile (64 x 656 B) are gathered with 16-byte loads
+//    into registers one tile ahead, then stored to LDS as a linear array,
+//    so consecutive lanes read consecutive 16 B of a record and write
+//    consecutive 16 B of LDS;
+//  * QK^T: wave w scores keys 16w..16w+15 of the tile for all 16 head rows
+//    with v_mfma_f32_16x16x32_bf16.  E4M3 codes are exact in bf16; each
+//    key's per-128 tile scale multiplies that tile's float32 partial, so the
+//    logits carry no rounding of code*scale (the pages' kernel applies its
+//    power-of-two scales to the operand instead);
+//  * the 16x64 logits go through LDS; every wave computes the online-softmax
+//    weights of the whole tile in the exp2 domain (scale * log2 e, as the
+//    FlyDSL launcher passes it) and keeps identical running max / sum;
+//  * PV: wave w owns latent tile w (128 columns) and computes
+//    O^T[d, h] += V^T[d, key] P^T[key, h]; P is multiplied by the key's
+//    scale of tile w before its bf16 rounding, and V^T comes straight from
+//    the record bytes in LDS with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b8), so each lane ends up owning one head;
+//  * rows longer than the launch needs are split over workgroups, whose
+//    float32 partials and base-2 LSEs are merged by merge_kernel.
+#include "device_utils.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kTileKeys = 64;
+constexpr int kThreads = 256;
+constexpr int kChunks = kRecordBytes / 16;                                // 41 x 16 B per record
+constexpr int kTileChunks = kTileKeys * kChunks;                          // 2624
+constexpr int kChunksPerThread = (kTileChunks + kThreads - 1) / kThreads;  // 11
+constexpr int kLogitPitch = kTileKeys + 4;                                 // floats per head row
+
+typedef __attribute__((address_space(3))) intx2_t lds_intx2_t;
+
+struct FwdKernelArgs {
+  const uint16_t *q;
+  int64_t q_st, q_sh;
+  const uint8_t *rec;
+  int64_t num_records;
+  const void *indptr;
+  const void *indices;
+  int64_t nnz;
+  float scale_log2;
+  int32_t heads;
+  int32_t splits;
+  uint16_t *out;
+  int64_t o_st, o_sh;
+  float *lse;
+  float *ws_out;
+  float *ws_lse;
+};
+
+template <typename IdxT, bool kSplit, bool kLse>
+__global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_rec[kTileKeys * kRecordBytes];
+  __shared__ __attribute__((aligned(16))) float s_logit[16 * kLogitPitch];
+  __shared__ __attribute__((aligned(16))) float s_scale[4 * kTileKeys];
+  __shared__ int s_slot[2][kTileKeys];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;  // MFMA row/column index of this lane
+  const int g = lane >> 4;  // MFMA k-group of this lane
+
+  const int64_t t = blockIdx.x / p.splits;
+  const int split = blockIdx.x - (int)(t * p.splits);
+
+  // ---- this workgroup's share of the row's CSR entries
+  const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
+  const IdxT *indices = static_cast<const IdxT *>(p.indices);
+  int64_t rb = (int64_t)indptr[t];
+  int64_t re = (int64_t)indptr[t + 1];
+  rb = rb < 0 ? 0 : (rb > p.nnz ? p.nnz : rb);
+  re = re < rb ? rb : (re > p.nnz ? p.nnz : re);
+  int64_t beg = rb, end = re;
+  if (kSplit) {
+    const int64_t per = (((re - rb) + p.splits - 1) / p.splits + kTileKeys - 1) & ~(int64_t)(kTileKeys - 1);
+    beg = rb + per * split;
+    beg = beg > re ? re : beg;
+    end = beg + per > re ? re : beg + per;
+  }
+  const int ntiles = (int)((end - beg + kTileKeys - 1) / kTileKeys);
+
+  // Slot of entry `tid` of tile `tile`, or -1 (masked, past the end, or
+  // outside the pool).
+  auto fetch_slot = [&](int tile) -> int {
+    int v = -1;
+    const int64_t e = beg + (int64_t)tile * kTileKeys + tid;
+    if (tile < ntiles && e < end) {
+      const int64_t x = (int64_t)indices[e];
+      if (x >= 0 && x < p.num_records) v = (int)x;
+    }
+    return v;
+  };
+
+  // ---- query fragments (MFMA A operand: row = head n, 8 k-slots per lane).
+  // Pair P < 8 covers latent d = 128*(P/2) + 64*(P%2) + 16*g + [0, 16);
+  // pair 8 covers rope d = 512 + 16*g + [0, 16).  Step 0 of a pair takes
+  // the first 8 of those 16 dims, step 1 the last 8; the record bytes are
+  // read with the same mapping, so the contraction covers every d once.
+  u32x4_t qf[9][2];
+  {
+    const uint32_t *qrow = reinterpret_cast<const uint32_t *>(p.q + t * p.q_st + (int64_t)n * p.q_sh);
+#pragma unroll
+    for (int P = 0; P < 9; ++P) {
+      const int d0 = P < 8 ? 128 * (P >> 1) + 64 * (P & 1) + 16 * g : 512 + 16 * g;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (n < p.heads) {
+          const uint32_t *src = qrow + ((d0 + 8 * st) >> 1);
+          v.x = src[0];
+          v.y = src[1];
+          v.z = src[2];
+          v.w = src[3];
+        }
+        qf[P][st] = v;
+      }
+    }
+  }
+
+  float m_run = -INFINITY;  // running max of head n's logits (exp2 domain)
+  float l_run = 0.f;        // this lane's part of head n's running sum
+  floatx4_t oacc[8];        // O^T[128*wave + 16*mt + 4*g + j][head n]
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t pf[kChunksPerThread];
+  auto issue_gather = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int c = tid + kThreads * i;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (c < kTileChunks) {
+        const int r = c / kChunks;
+        const int piece = c - r * kChunks;
+        const int slot = s_slot[buf][r];
+        if (slot >= 0)
+          v = *reinterpret_cast<const u32x4_t *>(p.rec + (int64_t)slot * kRecordBytes + piece * 16);
+      }
+      pf[i] = v;
+    }
+  };
+  auto store_gather = [&]() {
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int c = tid + kThreads * i;
+      if (c < kTileChunks) *reinterpret_cast<u32x4_t *>(s_rec + c * 16) = pf[i];
+    }
+  };
+
+  auto compute_tile = [&](int buf) {
+    // ---- QK^T for keys 16*wave + n
+    const uint8_t *krec = s_rec + (wave * 16 + n) * kRecordBytes;
+    const u32x4_t scv = *reinterpret_cast<const u32x4_t *>(krec + kScaleOffset);
+    floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ph = 0; ph < 2; ++ph) {
+        const u32x4_t c = *reinterpret_cast<const u32x4_t *>(krec + 128 * b + 64 * ph + 16 * g);
+        acc = mfma_16x16x32_bf16(as_bf16x8(qf[2 * b + ph][0]), e4m3x8_to_bf16x8(c.x, c.y), acc);
+        acc = mfma_16x16x32_bf16(as_bf16x8(qf[2 * b + ph][1]), e4m3x8_to_bf16x8(c.z, c.w), acc);
+      }
+      const float sc = as_float(scv[b]);
+      sacc += acc * sc;
+    }
+    {
+      const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g);
+      const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g + 16);
+      floatx4_t racc = {0.f, 0.f, 0.f, 0.f};
+      racc = mfma_16x16x32_bf16(as_bf16x8(qf[8][0]), as_bf16x8(r0), racc);
+      racc = mfma_16x16x32_bf16(as_bf16x8(qf[8][1]), as_bf16x8(r1), racc);
+      sacc += racc;
+    }
+    const bool valid = s_slot[buf][wave * 16 + n] >= 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s_logit[(4 * g + j) * kLogitPitch + wave * 16 + n] = valid ? sacc[j] * p.scale_log2 : -INFINITY;
+    s_scale[g * kTileKeys + wave * 16 + n] = as_float(scv[g]);
+    __syncthreads();
+
+    // ---- online softmax of head n over the tile; lane (n, g) holds keys
+    // 8g + [0, 8) and 32 + 8g + [0, 8) (the PV k-slots of this lane).
+    float sv[16];
+    {
+      const float *xr = s_logit + n * kLogitPitch;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const floatx4_t a = *reinterpret_cast<const floatx4_t *>(xr + 32 * ks + 8 * g);
+        const floatx4_t b = *reinterpret_cast<const floatx4_t *>(xr + 32 * ks + 8 * g + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sv[8 * ks + j] = a[j];
+          sv[8 * ks + 4 + j] = b[j];
+        }
+      }
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+    mt = fmaxf(mt, xor_shuffle(mt, 16));
+    mt = fmaxf(mt, xor_shuffle(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[i] = fast_exp2(sv[i] - m_ref);
+      psum += sv[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
+
+    // ---- P^T operands (B: column = head n, k-slot j = key 32ks + 8g + j),
+    // each weight times its key's scale for latent tile `wave`.
+    u32x4_t pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float *scp = s_scale + wave * kTileKeys + 32 * ks + 8 * g;
+      const floatx4_t s0 = *reinterpret_cast<const floatx4_t *>(scp);
+      const floatx4_t s1 = *reinterpret_cast<const floatx4_t *>(scp + 4);
+      pb[ks].x = pack_bf16x2(sv[8 * ks + 0] * s0[0], sv[8 * ks + 1] * s0[1]);
+      pb[ks].y = pack_bf16x2(sv[8 * ks + 2] * s0[2], sv[8 * ks + 3] * s0[3]);
+      pb[ks].z = pack_bf16x2(sv[8 * ks + 4] * s1[0], sv[8 * ks + 5] * s1[1]);
+      pb[ks].w = pack_bf16x2(sv[8 * ks + 6] * s1[2], sv[8 * ks + 7] * s1[3]);
+    }
+
+    // ---- PV.  In each 16-lane group g, lane n names record 32ks + 8g + n/2
+    // at column 128*wave + 16*mt + 8*(n&1); the transposing read hands lane
+    // n the bytes of column 128*wave + 16*mt + n of records 32ks + 8g + j,
+    // j = 0..7: the A operand row n, k-slots j.
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint8_t *vbase = s_rec + (32 * ks + 8 * g + (n >> 1)) * kRecordBytes + 128 * wave + 8 * (n & 1);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const intx2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2_t *)(vbase + 16 * m));
+        oacc[m] = mfma_16x16x32_bf16(e4m3x8_to_bf16x8((uint32_t)v.x, (uint32_t)v.y), as_bf16x8(pb[ks]), oacc[m]);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    int next_slot = -1;
+    if (tid < kTileKeys) {
+      s_slot[0][tid] = fetch_slot(0);
+      next_slot = fetch_slot(1);
+    }
+    __syncthreads();
+    issue_gather(0);
+    store_gather();
+    if (tid < kTileKeys) {
+      s_slot[1][tid] = next_slot;
+      next_slot = fetch_slot(2);
+    }
+    __syncthreads();
+    if (ntiles > 1) issue_gather(1);
+    for (int k = 0; k < ntiles; ++k) {
+      const int buf = k & 1;
+      compute_tile(buf);
+      __syncthreads();
+      if (k + 1 < ntiles) {
+        store_gather();  // tile k + 1
+        if (tid < kTileKeys) {
+          s_slot[buf][tid] = next_slot;  // tile k + 2
+          next_slot = fetch_slot(k + 3);
+        }
+        __syncthreads();
+        if (k + 2 < ntiles) issue_gather(buf);
+      }
+    }
+  }
+
+  // ---- epilogue: head n's total sum over the four k-groups
+  float l_tot = l_run + xor_shuffle(l_run, 16);
+  l_tot += xor_shuffle(l_tot, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const bool empty = m_run == -INFINITY;
+  if (n < p.heads) {
+    if (!kSplit) {
+      uint16_t *orow = p.out + t * p.o_st + (int64_t)n * p.o_sh + 128 * wave + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(orow + 16 * m);
+        dst[0] = pack_bf16x2(oacc[m][0] * inv, oacc[m][1] * inv);
+        dst[1] = pack_bf16x2(oacc[m][2] * inv, oacc[m][3] * inv);
+      }
+      if (kLse && wave == 0 && g == 0)
+        p.lse[t * p.heads + n] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    } else {
+      const int64_t row = (t * p.splits + split) * p.heads + n;
+      float *wo = p.ws_out + row * kLatent + 128 * wave + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) *reinterpret_cast<floatx4_t *>(wo + 16 * m) = oacc[m] * inv;
+      if (wave == 0 && g == 0) p.ws_lse[row] = empty ? -INFINITY : m_run + fast_log2(l_tot);
+    }
+  }
+}
+
+// Combine split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
+// One workgroup per (row, 4 heads); each thread owns 8 columns of one head.
+template <bool kLse>
+__global__ __launch_bounds__(256) void merge_kernel(const float *ws_out, const float *ws_lse, int32_t splits,
+                                                    int32_t heads, uint16_t *out, int64_t o_st, int64_t o_sh,
+                                                    float *lse) {
+  const int head_groups = (heads + 3) >> 2;
+  const int64_t t = blockIdx.x / head_groups;
+  const int h = (blockIdx.x - (int)(t * head_groups)) * 4 + (threadIdx.x >> 6);
+  const int col = (threadIdx.x & 63) * 8;
+  if (h >= heads) return;
+  const float *lp = ws_lse + t * splits * heads + h;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lp[(int64_t)s * heads]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float w = fast_exp2(lp[(int64_t)s * heads] - mx);
+      tot += w;
+      const float *o = ws_out + ((t * splits + s) * heads + h) * kLatent + col;
+      const floatx4_t a = *reinterpret_cast<const floatx4_t *>(o);
+      const floatx4_t b = *reinterpret_cast<const floatx4_t *>(o + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] += w * a[j];
+        acc[4 + j] += w * b[j];
+      }
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dst[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  if (kLse && col == 0) lse[t * heads + h] = mx == -INFINITY ? -INFINITY : (mx + fast_log2(tot)) * kLn2;
+}
+
+template <typename IdxT>
+hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
+  FwdKernelArgs k;
+  k.q = a.q;
+  k.q_st = a.q_stride_token;
+  k.q_sh = a.q_stride_head;
+  k.rec = a.records;
+  k.num_records = a.num_records;
+  k.indptr = a.indptr;
+  k.indices = a.indices;
+  k.nnz = a.num_indices;
+  k.scale_log2 = a.scale_log2;
+  k.heads = a.num_heads;
+  k.splits = a.splits;
+  k.out = a.out;
+  k.o_st = a.out_stride_token;
+  k.o_sh = a.out_stride_head;
+  k.lse = a.lse;
+  k.ws_out = a.ws_out;
+  k.ws_lse = a.ws_lse;
+  const dim3 block(kThreads);
+  const dim3 grid((unsigned)((int64_t)a.num_tokens * a.splits));
+  const bool lse = a.lse != nullptr;
+  if (a.splits <= 1) {
+    if (lse)
+      sparse_fwd_kernel<IdxT, false, true><<<grid, block, 0, stream>>>(k);
+    else
+      sparse_fwd_kernel<IdxT, false, false><<<grid, block, 0, stream>>>(k);
+    return hipGetLastError();
+  }
+  sparse_fwd_kernel<IdxT, true, false><<<grid, block, 0, stream>>>(k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 mgrid((unsigned)((int64_t)a.num_tokens * ((a.num_heads + 3) / 4)));
+  if (lse)
+    merge_kernel<true><<<mgrid, 256, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
+                                                  a.out_stride_token, a.out_stride_head, a.lse);
+  else
+    merge_kernel<false><<<mgrid, 256, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
+                                                   a.out_stride_token, a.out_stride_head, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_fwd(const FwdArgs &a, hipStream_t stream) {
+  return a.index_i64 ? launch_typed<int64_t>(a, stream) : launch_typed<int32_t>(a, stream);
+}
+
+}  // namespace mla

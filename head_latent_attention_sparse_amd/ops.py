@@ -1,0 +1,221 @@
+"""Thin Python binding over libmla.so (ctypes).
+
+Argument marshalling only: tensors are turned into pointers, sizes and
+strides, and every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory (outputs, the split-KV workspace)
+and the current stream.  There is no fallback: if libmla.so is missing or
+fails to load, every call raises.
+
+Names and keyword arguments follow flydsl_sparse_mla_fp8ds_fwd on the
+flydsl_sparse_mla page and the ds_mla insert on the
+fused_mla_key_concat_kv_cache page.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+
+RECORD_BYTES = 656
+KV_LORA_RANK = 512
+QK_ROPE_HEAD_DIM = 64
+MAX_HEADS = 16
+MAX_SPLITS = 1024
+
+FLAG_HAS_INVALID = 1 << 0
+FLAG_RETURN_LSE = 1 << 1
+FLAG_INDEX_I64 = 1 << 2
+SPLITS_SHIFT = 16
+
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_HIP",
+          4: "MLA_ERR_OUT_OF_MEMORY"}
+
+# Exported entry points and their C signatures (include/mla.h).
+_I64, _I32, _U32, _F32, _P, _SZ = (ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float,
+                                   ctypes.c_void_p, ctypes.c_size_t)
+SIGNATURES = {
+    "mla_sparse_fwd": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P, _I64, _I64,
+                              _P, _P, _SZ, _P]),
+    "mla_sparse_fwd_num_splits": (_I32, [_I64, _I64, _I32, _U32]),
+    "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
+    "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
+    "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "mla_last_error": (ctypes.c_char_p, []),
+    "mla_status_string": (ctypes.c_char_p, [_I32]),
+    "mla_abi_version": (_I32, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded library with its C signatures set (raises if it cannot load)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m head_latent_attention_sparse_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def _check(status, unsupported_is_value_error=True):
+    if status == 0:
+        return
+    msg = lib().mla_last_error().decode()
+    if status in (1, 2) and unsupported_is_value_error:
+        raise ValueError(f"{STATUS[status]}: {msg}")
+    raise MlaError(status, msg)
+
+
+def _kv_rows(kv):
+    """(base pointer, number of records, record pitch) of a record pool view.
+
+    Takes [N, 656], [N, 1, 656], [N, 1, 1, 656] or an unpadded paged pool
+    [nb, block, 656] of any 1-byte dtype (the views the flydsl_sparse_mla
+    page's ``_kv_rows`` accepts).  A layout that is not flat records yields a
+    pitch other than 656, which the library rejects.
+    """
+    if not torch.is_tensor(kv) or kv.element_size() != 1 or kv.ndim not in (2, 3, 4):
+        raise ValueError("kv cache must be a 1-byte tensor of rank 2, 3 or 4")
+    if kv.shape[-1] != RECORD_BYTES or kv.stride(-1) != 1:
+        raise ValueError("kv cache rows must be 656 contiguous bytes")
+    if kv.ndim == 4 and (kv.shape[1] != 1 or kv.shape[2] != 1):
+        raise ValueError("a 4-D kv cache must be [N, 1, 1, 656]")
+    n = kv.numel() // RECORD_BYTES
+    if kv.ndim == 3 and kv.shape[1] != 1:
+        pitch = kv.stride(1)
+        if kv.shape[0] > 1 and kv.stride(0) != kv.shape[1] * pitch:
+            pitch = kv.stride(0)  # padded pages: rejected by the library
+    else:
+        pitch = kv.stride(0) if kv.shape[0] > 1 else RECORD_BYTES
+    return kv.data_ptr(), n, pitch
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def num_splits(num_tokens, num_indices, num_cus, forced=0):
+    """The split-KV count the library picks (host only)."""
+    return lib().mla_sparse_fwd_num_splits(num_tokens, num_indices, num_cus, forced << SPLITS_SHIFT)
+
+
+def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid=False, out=None,
+               return_lse=False, num_splits=0, workspace=None):
+    """Sparse MLA forward over fp8_ds_mla records -> (out, lse or None).
+
+    q [T, H, 576] bf16 (H <= 16, stride(2) == 1); kv_cache a record pool
+    view; kv_indptr [T + 1] and kv_indices [nnz] int32 or int64 (the same
+    dtype, contiguous); out optional [T, H, >= 512] bf16.  ``num_splits``
+    forces the split-KV count (0 = the library's choice).  ``workspace``
+    optionally supplies the split partial buffer (a CUDA uint8 tensor).
+    """
+    if not (torch.is_tensor(q) and q.is_cuda and q.ndim == 3 and q.dtype == torch.bfloat16):
+        raise ValueError("q must be a CUDA bf16 tensor [T, H, 576]")
+    t_count, heads, dqk = q.shape
+    if dqk != KV_LORA_RANK + QK_ROPE_HEAD_DIM or q.stride(2) != 1:
+        raise ValueError("q rows must be 576 contiguous bf16 values")
+    if not 1 <= heads <= MAX_HEADS:
+        raise ValueError(f"{heads} heads: 1 .. {MAX_HEADS} are served")
+    for name, x in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices)):
+        if not (torch.is_tensor(x) and x.device == q.device and x.ndim == 1 and x.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 1-D tensor on q's device")
+        if x.dtype not in (torch.int32, torch.int64):
+            raise ValueError(f"{name} must be int32 or int64")
+    if kv_indptr.dtype != kv_indices.dtype:
+        raise ValueError("kv_indptr and kv_indices must have the same dtype")
+    if kv_indptr.numel() != t_count + 1:
+        raise ValueError("kv_indptr must have T + 1 entries")
+    if not (torch.is_tensor(kv_cache) and kv_cache.device == q.device):
+        raise ValueError("kv cache must be on q's device")
+    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    if out is None:
+        out = torch.empty((t_count, heads, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
+    else:
+        if not (out.dtype == torch.bfloat16 and out.device == q.device and out.ndim == 3
+                and out.shape[0] == t_count and out.shape[1] == heads and out.shape[2] >= KV_LORA_RANK
+                and out.stride(2) == 1):
+            raise ValueError("out must be bf16 [T, H, >= 512] with stride(2) == 1 on q's device")
+    lse = torch.empty((t_count, heads), dtype=torch.float32, device=q.device) if return_lse else None
+    flags = (FLAG_HAS_INVALID if has_invalid else 0) | (FLAG_RETURN_LSE if return_lse else 0)
+    if kv_indices.dtype == torch.int64:
+        flags |= FLAG_INDEX_I64
+    if not 0 <= num_splits <= MAX_SPLITS:
+        raise ValueError(f"num_splits must be in 0 .. {MAX_SPLITS}")
+    flags |= num_splits << SPLITS_SHIFT
+    L = lib()
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    with torch.cuda.device(dev):
+        ws_ptr, ws_bytes = None, 0
+        if t_count > 0:
+            need = L.mla_sparse_fwd_workspace_size(t_count, heads, kv_indices.numel(), flags, dev)
+            if need == ctypes.c_size_t(-1).value:
+                _check(3)
+            if need > 0:
+                if workspace is None:
+                    workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                if workspace.numel() < need:
+                    raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+                ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+        st = L.mla_sparse_fwd(
+            q.data_ptr(), t_count, heads, q.stride(0), q.stride(1),
+            kv_ptr, n_rec, pitch,
+            kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None, kv_indices.numel(),
+            float(softmax_scale), flags,
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr() if lse is not None else None,
+            ws_ptr, ws_bytes, _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def cache_insert(kv_c, k_pe, slot_mapping, kv_cache):
+    """Quantize [kv_c | k_pe] of each token into its record (in place).
+
+    kv_c [Tn, 512] bf16 (stride(1) == 1); k_pe [Tn, 64] or [Tn, 1, 64] bf16;
+    slot_mapping [Tn] int64 (negative = skip); kv_cache a record pool view.
+    """
+    if not (torch.is_tensor(kv_c) and kv_c.is_cuda and kv_c.dtype == torch.bfloat16 and kv_c.ndim == 2
+            and kv_c.shape[1] == KV_LORA_RANK and kv_c.stride(1) == 1):
+        raise ValueError("kv_c must be a CUDA bf16 [T, 512] tensor with stride(1) == 1")
+    n = kv_c.shape[0]
+    if not (torch.is_tensor(k_pe) and k_pe.dtype == torch.bfloat16 and k_pe.device == kv_c.device
+            and k_pe.shape[0] == n):
+        raise ValueError("k_pe must be bf16 [T, 64] or [T, 1, 64] on kv_c's device")
+    if k_pe.numel() != n * QK_ROPE_HEAD_DIM:
+        raise ValueError("k_pe must hold 64 values per token")
+    k_pe2 = k_pe.reshape(n, QK_ROPE_HEAD_DIM)
+    if k_pe2.shape[1] != QK_ROPE_HEAD_DIM or k_pe2.stride(1) != 1:
+        raise ValueError("k_pe rows must be 64 contiguous bf16 values")
+    if not (torch.is_tensor(slot_mapping) and slot_mapping.dtype == torch.int64 and slot_mapping.ndim == 1
+            and slot_mapping.numel() == n and slot_mapping.is_contiguous()
+            and slot_mapping.device == kv_c.device):
+        raise ValueError("slot_mapping must be a contiguous int64 [T] tensor on kv_c's device")
+    if not (torch.is_tensor(kv_cache) and kv_cache.device == kv_c.device):
+        raise ValueError("kv cache must be on kv_c's device")
+    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    L = lib()
+    with torch.cuda.device(kv_c.device):
+        st = L.mla_cache_insert(kv_c.data_ptr(), kv_c.stride(0), k_pe2.data_ptr(), k_pe2.stride(0),
+                                slot_mapping.data_ptr(), n, kv_ptr, n_rec, pitch, _stream(kv_c.device))
+    _check(st)
+    return kv_cache

@@ -1,0 +1,189 @@
+/*
+ * mla.h - sparse absorbed multi-head latent attention (MLA) over an
+ * fp8_ds_mla latent cache, for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer unless stated
+ * otherwise; the caller owns every buffer and the stream.  No call
+ * synchronizes the host: work is queued on `stream` (a hipStream_t passed
+ * as void*, NULL = the default stream) and the call returns.
+ *
+ * Record format (vLLM API pages, flydsl_sparse_mla module docstring and
+ * flydsl_sparse_mla_fp8ds_supported docstring; fused_mla_key_concat_kv_cache
+ * page, fused_mla_key_concat_ds_mla_insert docstring): one 656-byte record
+ * per cache slot,
+ *     bytes   0 .. 511  latent d = 0..511 as OCP E4M3 ("e4m3fn")
+ *     bytes 512 .. 527  4 little-endian float32 scales; scale b covers
+ *                       latent [128b, 128b + 128)
+ *     bytes 528 .. 655  64 little-endian bf16 rope values
+ * latent[d] = e4m3(byte d) * scale[d / 128].  Slot s is record s of the
+ * pool; for an unpadded paged pool [num_blocks, block_size, 656] that is
+ * block s / block_size, offset s % block_size.
+ *
+ * Errors: a call that returns anything but MLA_OK has queued nothing and
+ * written nothing; mla_last_error() then holds a message for the calling
+ * thread.  Validation reads argument values only (no device reads), so a
+ * rejected call is safe at any time, including during stream capture.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* NULL / misaligned pointer, negative size or stride, bad flag bits */
+  MLA_ERR_UNSUPPORTED = 2,      /* well-formed, but outside what the library serves */
+  MLA_ERR_HIP = 3,              /* a HIP runtime call or a kernel launch failed */
+  MLA_ERR_OUT_OF_MEMORY = 4     /* the library-owned split-KV workspace could not be allocated */
+} mla_status_t;
+
+#define MLA_RECORD_BYTES 656
+#define MLA_KV_LORA_RANK 512
+#define MLA_ROPE_DIM 64
+#define MLA_QK_DIM 576
+#define MLA_MAX_HEADS 16
+#define MLA_MAX_INDICES (1 << 29) /* num_indices must be below this */
+#define MLA_MAX_SPLITS 1024
+
+/* mla_sparse_fwd flags */
+#define MLA_FLAG_HAS_INVALID (1u << 0) /* negative slot ids may occur (they are masked either way) */
+#define MLA_FLAG_RETURN_LSE (1u << 1)  /* write lse */
+#define MLA_FLAG_INDEX_I64 (1u << 2)   /* kv_indptr and kv_indices are int64 (default int32) */
+/* Force the split-KV count to n (1 .. MLA_MAX_SPLITS); 0 = chosen by the library. */
+#define MLA_FLAG_SPLITS(n) (((uint32_t)(n)) << 16)
+#define MLA_FLAG_SPLITS_MASK (0xFFFFu << 16)
+
+/*
+ * mla_sparse_fwd - sparse attention of absorbed MLA queries over records.
+ *
+ * Defined by the flydsl_sparse_mla page (flydsl_sparse_mla_fp8ds_fwd
+ * docstring; the argument limits of flydsl_sparse_mla_fp8ds_supported):
+ * for query row t and head h, with J the entries of
+ * kv_indices[kv_indptr[t] .. kv_indptr[t+1]) that are >= 0 (and, in this
+ * library, < num_records),
+ *     k_j = [latent_j | rope_j] (576),   v_j = latent_j (512),
+ *     z_j = softmax_scale * <q[t,h,:], k_j>,
+ *     out[t,h,:] = sum_j softmax(z)_j v_j      (bf16, round to nearest even),
+ *     lse[t,h]   = ln sum_j exp(z_j)           (float32, natural log).
+ * A row with no such entry gives out = 0 and lse = -inf.  A slot listed
+ * twice counts twice.  Rows of many keys are split over several workgroups
+ * (split-KV) whose float32 partials are combined by their LSEs in a second
+ * launch, the merge named by merge_attn_states on the kimi_k3 nvidia mla
+ * page.
+ *
+ *  q            bf16 [num_tokens, num_heads, 576], element (t,h,d) at
+ *               q + t*q_stride_token + h*q_stride_head + d (strides in
+ *               elements, even, >= 0; base 4-byte aligned).
+ *  num_tokens   T >= 0.  T == 0 returns MLA_OK and queues nothing.
+ *  num_heads    1 .. 16 (else MLA_ERR_UNSUPPORTED).
+ *  kv_records   uint8 records, base 16-byte aligned; num_records >= 0
+ *               records at record_stride bytes (must be 656: a padded
+ *               page pitch is MLA_ERR_UNSUPPORTED).  Addressed in 64 bits.
+ *  kv_indptr    [T + 1] int32 (int64 with MLA_FLAG_INDEX_I64) CSR offsets
+ *               into kv_indices, non-decreasing; offsets are clamped to
+ *               [0, num_indices] on the device.
+ *  kv_indices   [num_indices] int32 (int64 with MLA_FLAG_INDEX_I64) slot ids;
+ *               0 <= num_indices < 2^29; may be NULL when num_indices == 0.
+ *  softmax_scale  the layer's scale (used as this float32).
+ *  flags        MLA_FLAG_* bits; unknown bits are MLA_ERR_INVALID_ARGUMENT.
+ *  out          bf16, element (t,h,d) at out + t*out_stride_token +
+ *               h*out_stride_head + d for d < 512 (rows may be wider; only
+ *               the first 512 columns are written); strides even, >= 0;
+ *               base 4-byte aligned.
+ *  lse          float32 [T, num_heads] contiguous; required with
+ *               MLA_FLAG_RETURN_LSE, ignored otherwise.
+ *  workspace    scratch for split-KV partials of at least
+ *               mla_sparse_fwd_workspace_size(...) bytes, 256-byte aligned,
+ *               or NULL: the library then uses a buffer it owns per device
+ *               (allocated on first need, grown when too small; growing
+ *               calls hipMalloc, so call mla_workspace_reserve before
+ *               stream capture).  The buffer must not be used by another
+ *               call that may run at the same time.
+ *  stream       hipStream_t as void*.
+ * Returns MLA_OK when the work is queued.
+ */
+mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads,
+                            int64_t q_stride_token, int64_t q_stride_head,
+                            const void *kv_records, int64_t num_records, int64_t record_stride,
+                            const void *kv_indptr, const void *kv_indices, int64_t num_indices,
+                            float softmax_scale, uint32_t flags,
+                            void *out, int64_t out_stride_token, int64_t out_stride_head,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mla_sparse_fwd_num_splits - the split-KV count mla_sparse_fwd uses (host
+ * only, no device access).  It depends on T, num_indices, the device's
+ * compute-unit count and the forced count in flags, never on index values:
+ * the count is fixed by a bound known on the host, as the split counts of
+ * the decode cores on the kimi_k3 specialized-decode page are
+ * (PreparedMla.fill_splits / max_seq).  Returns 0 for invalid arguments.
+ */
+int32_t mla_sparse_fwd_num_splits(int64_t num_tokens, int64_t num_indices, int32_t num_cus,
+                                  uint32_t flags);
+
+/*
+ * mla_sparse_fwd_workspace_size - bytes of split-KV workspace a call with
+ * these arguments needs on device `device` (0 when it does not split).
+ * Host only; queries the device's compute-unit count once.
+ * Returns (size_t)-1 on error (see mla_last_error).
+ */
+size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_indices,
+                                     uint32_t flags, int device);
+
+/*
+ * mla_workspace_reserve - grow the library-owned workspace of `device` to at
+ * least `bytes` now (it never shrinks).  Call before stream capture.
+ */
+mla_status_t mla_workspace_reserve(int device, size_t bytes);
+
+/*
+ * mla_cache_insert - quantize tokens' [kv_c_normed | k_pe] into records.
+ *
+ * The ds_mla insert of fused_mla_key_concat_ds_mla_insert and of
+ * fused_mla_decode_q_concat_kv_cache_insert(ds_mla=True)
+ * (fused_mla_key_concat_kv_cache page): for token i with
+ * p = slot_mapping[i] >= 0, record p becomes, per 128-wide tile b,
+ *     scale_b = max_d |kv_c[i, 128b + d]| / 448        (float32, correctly rounded)
+ *     code[d] = E4M3(clamp(kv_c[i, d] / scale_b, -448, 448))
+ *               (float32 correctly rounded division, round to nearest even;
+ *                a tile of zeros gets scale 0 and codes 0)
+ * followed by the 64 bf16 rope values k_pe[i, :] copied bit for bit.
+ * Tokens with a negative slot, or a slot >= num_records, are skipped and
+ * their records keep their bytes.  Two tokens with the same slot in one
+ * call race (undefined which one lands).
+ *
+ *  kv_c         bf16 [num_tokens, 512], row stride kv_c_stride_token
+ *               elements (even), base 4-byte aligned.
+ *  k_pe         bf16 [num_tokens, 64], row stride k_pe_stride_token
+ *               elements (even), base 4-byte aligned.
+ *  slot_mapping int64 [num_tokens], 8-byte aligned.
+ *  num_tokens   >= 0; 0 returns MLA_OK and queues nothing.
+ *  kv_records   as for mla_sparse_fwd (written in place).
+ */
+mla_status_t mla_cache_insert(const void *kv_c, int64_t kv_c_stride_token,
+                              const void *k_pe, int64_t k_pe_stride_token,
+                              const int64_t *slot_mapping, int64_t num_tokens,
+                              void *kv_records, int64_t num_records, int64_t record_stride,
+                              void *stream);
+
+/* Message for the last failed call on this thread ("" if none).  Host memory
+ * owned by the library, valid until the thread's next failing call. */
+const char *mla_last_error(void);
+
+/* Static name of a status code. */
+const char *mla_status_string(mla_status_t status);
+
+/* ABI version of this header (MLA_ABI_VERSION). */
+#define MLA_ABI_VERSION 1
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,156 @@
+"""The C-ABI library loads, exports what include/mla.h declares, and rejects
+bad arguments on the host (no GPU: no call here reaches a kernel).
+
+Validation reads argument values only, so every rejection is checkable with
+placeholder pointer values; the clauses mirror the limits
+flydsl_sparse_mla_fp8ds_supported states on the flydsl_sparse_mla page.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_latent_attention_sparse_amd as mla
+from head_latent_attention_sparse_amd import ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+A = 0x100000  # a 256-byte aligned placeholder address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(ops.SIGNATURES), names
+    lib = mla.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define MLA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert mla.lib().mla_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    lib = mla.lib()
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_status_string(2) == b"MLA_ERR_UNSUPPORTED"
+
+
+def fwd(**kw):
+    args = dict(q=A, T=4, H=16, qst=16 * 576, qsh=576, kv=A, n=100, pitch=656, indptr=A, indices=A, nnz=10,
+                scale=1.0, flags=2, out=A, ost=16 * 512, osh=512, lse=A, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_sparse_fwd(args["q"], args["T"], args["H"], args["qst"], args["qsh"], args["kv"], args["n"],
+                            args["pitch"], args["indptr"], args["indices"], args["nnz"], args["scale"], args["flags"],
+                            args["out"], args["ost"], args["osh"], args["lse"], args["ws"], args["wsb"],
+                            args["stream"])
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=0), UNSUPPORTED),
+    (dict(H=17), UNSUPPORTED),
+    (dict(T=-1), INVALID),
+    (dict(qst=16 * 576 + 1), UNSUPPORTED),
+    (dict(qsh=577), UNSUPPORTED),
+    (dict(ost=8191), UNSUPPORTED),
+    (dict(osh=-2), INVALID),
+    (dict(q=A + 2), UNSUPPORTED),
+    (dict(out=A + 2), UNSUPPORTED),
+    (dict(kv=A + 8), UNSUPPORTED),
+    (dict(pitch=672), UNSUPPORTED),
+    (dict(pitch=64 * 672), UNSUPPORTED),
+    (dict(n=-1), INVALID),
+    (dict(nnz=1 << 29), UNSUPPORTED),
+    (dict(nnz=-3), INVALID),
+    (dict(flags=1 << 7), INVALID),
+    (dict(flags=2, lse=None), INVALID),
+    (dict(lse=A + 1), INVALID),
+    (dict(indptr=A + 2), INVALID),
+    (dict(flags=2 | 4, indices=A + 4), INVALID),
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(indptr=None), INVALID),
+    (dict(indices=None), INVALID),
+])
+def test_fwd_rejections(kw, status):
+    st, msg = fwd(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_fwd_zero_tokens_is_a_no_op():
+    st, _ = fwd(T=0, q=None, out=None, indptr=None, indices=None, lse=None)
+    assert st == OK
+
+
+def insert(**kw):
+    args = dict(kv_c=A, kst=512, k_pe=A, pst=64, slots=A, T=8, kv=A, n=100, pitch=656, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_cache_insert(args["kv_c"], args["kst"], args["k_pe"], args["pst"], args["slots"], args["T"],
+                              args["kv"], args["n"], args["pitch"], args["stream"])
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), INVALID),
+    (dict(kst=511), UNSUPPORTED),
+    (dict(pst=-64), INVALID),
+    (dict(pitch=660), UNSUPPORTED),
+    (dict(kv=A + 4), UNSUPPORTED),
+    (dict(kv_c=A + 2), UNSUPPORTED),
+    (dict(k_pe=A + 1), UNSUPPORTED),
+    (dict(slots=A + 4), INVALID),
+    (dict(n=-5), INVALID),
+    (dict(kv_c=None), INVALID),
+    (dict(slots=None), INVALID),
+])
+def test_insert_rejections(kw, status):
+    st, msg = insert(**kw)
+    assert st == status, msg
+
+
+def test_insert_zero_tokens_is_a_no_op():
+    st, _ = insert(T=0, kv_c=None, k_pe=None, slots=None)
+    assert st == OK
+
+
+@pytest.mark.parametrize("tokens,nnz,cus,forced,want", [
+    (4096, 4096 * 2048, 256, 0, 1),     # sparse prefill: enough rows
+    (1024, 1024 * 1024, 256, 0, 1),     # insert + attend
+    (4, 512, 256, 0, 1),                # tiny rows: no split
+    (8, 8 * 131072, 256, 0, 64),        # long context: 512 workgroups
+    (64, 64 * 4608, 256, 0, 8),         # paged decode
+    (8, 8 * 131072, 256, 7, 7),         # forced
+    (8, 100, 256, 5000, 1024),          # forced, clamped
+    (0, 0, 256, 0, 1),
+])
+def test_split_plan(tokens, nnz, cus, forced, want):
+    assert mla.num_splits(tokens, nnz, cus, forced) == want
+
+
+def test_split_plan_depends_only_on_host_values():
+    lib = mla.lib()
+    assert lib.mla_sparse_fwd_num_splits(-1, 0, 256, 0) == 0
+    assert lib.mla_sparse_fwd_num_splits(8, 0, 256, 1 << 5) == 0  # unknown flag bit
+
+
+def test_workspace_size_of_forced_split_needs_no_device():
+    lib = mla.lib()
+    size = lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 4 << 16, 0)
+    rows = 8 * 4 * 16
+    assert size == ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 1 << 16, 0) == 0
+    assert lib.mla_sparse_fwd_workspace_size(8, 17, 1000, 4 << 16, 0) == ctypes.c_size_t(-1).value

@@ -1,0 +1,321 @@
+"""GPU parity of mla_sparse_fwd against the fp64 oracle.
+
+Bar (spec tolerance): |out - ref| <= 1e-2 + 1e-2 |ref| elementwise,
+|lse - ref| <= 2e-3, -inf exactly where the oracle has an empty row.  The
+GPU pools are built by mla_cache_insert and first checked byte for byte
+against the oracle's writer; the oracle works from its own records.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_sparse_amd as mla
+from head_latent_attention_sparse_amd import workloads
+from head_latent_attention_sparse_amd.workloads import InsertBatch, bf16_bits
+from oracle import decode_records, sparse_fwd as oracle_fwd
+from tests.helpers import (assert_fwd_close, oracle_encode, oracle_subpool, remap_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def build_gpu_pool(w, with_step=True):
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=DEV)
+    view = pool.view(-1, w.block_size, 656) if w.block_size else pool
+    for b in w.setup_inserts + (w.step_inserts if with_step else []):
+        mla.cache_insert(b.kv_c.to(DEV), b.k_pe.to(DEV), b.slots.to(DEV), view)
+    return pool, view
+
+
+def run_gpu(w, view, rows_out=None, **kw):
+    q = w.q.to(DEV)
+    out, lse = mla.sparse_fwd(q, view, w.indptr.to(DEV), w.indices.to(DEV), w.softmax_scale,
+                              has_invalid=w.has_invalid, return_lse=w.return_lse, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_rows(w, pool, out, lse, rows, what):
+    """Oracle on the listed rows (sub-pool of the slots they use)."""
+    indptr, indices = w.indptr.numpy(), w.indices.numpy()
+    needed = np.concatenate([indices[indptr[t]:indptr[t + 1]] for t in rows]) if len(rows) else np.zeros(0)
+    batches = w.setup_inserts + w.step_inserts
+    uniq, sub = oracle_subpool(w.num_records, batches, needed)
+    # the GPU pool holds the oracle's bytes for these slots
+    got = pool[torch.from_numpy(uniq).to(DEV)].cpu().numpy() if uniq.size else sub
+    assert np.array_equal(got, sub), f"{what}: inserted records differ from the oracle writer"
+    ptr, ind = remap_rows(indptr, indices, rows, uniq, w.num_records)
+    q_bits = bf16_bits(w.q)[list(rows)]
+    ref_out, ref_lse = oracle_fwd(q_bits, sub, ptr, ind, w.softmax_scale)
+    sel = torch.tensor(list(rows), dtype=torch.long, device=DEV)
+    assert_fwd_close(out[sel], lse[sel] if lse is not None else None, ref_out,
+                     ref_lse if lse is not None else None, what)
+
+
+def check_all_rows_sane(w, out, lse):
+    """Properties at any size: empty rows give 0 / -inf, the rest finite."""
+    indptr, indices = w.indptr.numpy().astype(np.int64), w.indices.numpy().astype(np.int64)
+    ok = (indices >= 0) & (indices < w.num_records)
+    counts = np.add.reduceat(ok.astype(np.int64), indptr[:-1]) if indices.size else np.zeros(w.num_tokens, np.int64)
+    counts[indptr[:-1] == indptr[1:]] = 0
+    empty = torch.from_numpy(counts == 0).to(DEV)
+    assert torch.isfinite(out.float()).all()
+    if lse is not None:
+        assert torch.equal(torch.isneginf(lse).any(dim=1), empty)
+        assert torch.isfinite(lse[~empty]).all()
+    assert (out[empty] == 0).all()
+
+
+# ----------------------------------------------------------------- configs
+
+def test_config1_tiny_all_rows():
+    say("fwd config1 tiny")
+    w = workloads.tiny()
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_rows(w, pool, out, lse, range(w.num_tokens), "config1")
+
+
+def test_config2_paged_decode_reduced():
+    say("fwd config2 reduced (8 requests)")
+    w = workloads.paged_decode(batch=8)
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_rows(w, pool, out, lse, range(8), "config2-reduced")
+
+
+def test_config2_paged_decode_full_sampled():
+    say("fwd config2 full, 6 sampled rows")
+    w = workloads.paged_decode()
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, [0, 9, 21, 37, 50, 63], "config2-full")
+
+
+def test_config3_sparse_prefill_reduced():
+    say("fwd config3 reduced (T=96, N=16384)")
+    w = workloads.sparse_prefill(tokens=96, records=16384, frac_empty=0.03)
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, range(96), "config3-reduced")
+
+
+def test_config3_sparse_prefill_full_sampled():
+    say("fwd config3 full (T=4096, N=131072), sampled rows")
+    w = workloads.sparse_prefill()
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    indptr, ind = w.indptr.numpy(), w.indices.numpy()
+    empty = [t for t in range(w.num_tokens) if np.all(ind[indptr[t]:indptr[t + 1]] < 0)]
+    assert len(empty) == 41
+    rows = sorted(set([0, 1, 777, 2048, 3333, 4095] + empty[:2]))
+    check_rows(w, pool, out, lse, rows, "config3-full")
+
+
+def test_config4_long_context_reduced():
+    say("fwd config4 reduced (T=3, N=20000): automatic split-KV")
+    w = workloads.long_context(tokens=3, records=20000)
+    assert mla.num_splits(3, w.nnz, torch.cuda.get_device_properties(0).multi_processor_count) > 1
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_rows(w, pool, out, lse, range(3), "config4-reduced")
+
+
+def test_config4_long_context_full_sampled():
+    say("fwd config4 full (T=8, N=131072), 2 sampled rows")
+    w = workloads.long_context()
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, [0, 5], "config4-full")
+
+
+def test_config5_insert_attend_full_sampled():
+    say("fwd config5 full: insert then attend, 12 sampled rows")
+    w = workloads.insert_attend()
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, list(range(0, 1024, 93)), "config5-full")
+
+
+# ----------------------------------------------------------------- sweeps and edges
+
+def small_workload(seed, tokens, heads, records, lengths, p_invalid=0.0, latent_std=1.0, dup=False):
+    g = torch.Generator().manual_seed(seed)
+    kv_c = (torch.randn((records, 512), generator=g) * latent_std).to(torch.bfloat16)
+    k_pe = torch.randn((records, 64), generator=g).to(torch.bfloat16)
+    q = torch.randn((tokens, heads, 576), generator=g).to(torch.bfloat16)
+    rows = []
+    for t in range(tokens):
+        n = lengths[t % len(lengths)]
+        r = torch.randint(0, records, (n,), generator=g) if dup else torch.randperm(records, generator=g)[:n]
+        r = r.to(torch.int64)
+        r[torch.rand(n, generator=g) < p_invalid] = -1
+        rows.append(r)
+    indptr = torch.tensor([0] + [len(r) for r in rows]).cumsum(0).to(torch.int32)
+    indices = torch.cat(rows).to(torch.int32) if rows else torch.zeros(0, dtype=torch.int32)
+    fill = InsertBatch(kv_c, k_pe, torch.arange(records, dtype=torch.int64))
+    return workloads.Workload("small", records, q, indptr, indices, 192**-0.5, p_invalid > 0, True,
+                              setup_inserts=[fill])
+
+
+@pytest.mark.parametrize("heads", [1, 2, 4, 6, 8, 12, 16])
+@pytest.mark.parametrize("has_invalid", [False, True])
+@pytest.mark.parametrize("return_lse", [False, True])
+def test_heads_sweep(heads, has_invalid, return_lse):
+    say(f"fwd heads={heads} has_invalid={has_invalid} return_lse={return_lse}")
+    w = small_workload(300 + heads, 5, heads, 600, [0, 1, 65, 130, 300], p_invalid=0.2 if has_invalid else 0.0)
+    w.return_lse = return_lse
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    assert (lse is None) == (not return_lse)
+    check_rows(w, pool, out, lse, range(5), f"H={heads}")
+
+
+def test_warmup_problem(golden_dir):
+    say("fwd warmup problem")
+    with open(os.path.join(golden_dir, "warmup_problem.json")) as f:
+        fx = json.load(f)
+    kv = torch.zeros((1, 656), dtype=torch.uint8, device=DEV)
+    indptr = torch.tensor(fx["indptr"], dtype=torch.int32, device=DEV)
+    indices = torch.tensor(fx["indices"], dtype=torch.int32, device=DEV)
+    for heads in fx["heads"]:
+        for hi in (False, True):
+            q = torch.zeros((1, heads, 576), dtype=torch.bfloat16, device=DEV)
+            out, lse = mla.sparse_fwd(q, kv, indptr, indices, fx["softmax_scale"], has_invalid=hi, return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.all(out.float() == fx["expected_out"])
+            assert torch.all(lse == fx["expected_lse"])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_forced_splits(splits):
+    say(f"fwd forced splits={splits}")
+    w = small_workload(400, 4, 16, 3000, [2500, 700, 64, 0], p_invalid=0.1, latent_std=2.0)
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view, num_splits=splits)
+    check_rows(w, pool, out, lse, range(4), f"splits={splits}")
+
+
+def test_ragged_lengths_int32_and_int64():
+    say("fwd ragged lengths, int32 and int64 indices")
+    lengths = [0, 1, 2, 63, 64, 65, 127, 128, 129, 191, 257]
+    w = small_workload(500, len(lengths), 16, 1000, lengths)
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_rows(w, pool, out, lse, range(len(lengths)), "ragged-i32")
+    out64, lse64 = mla.sparse_fwd(w.q.to(DEV), view, w.indptr.to(torch.int64).to(DEV),
+                                  w.indices.to(torch.int64).to(DEV), w.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out64, out) and torch.equal(lse64, lse)
+
+
+def test_masked_out_of_range_and_duplicate_slots():
+    say("fwd masked / out-of-range / duplicate slots")
+    w = small_workload(600, 6, 12, 400, [90, 40, 200], dup=True, p_invalid=0.15)
+    ind = w.indices.clone()
+    ind[3::17] = 400 + 5  # outside the pool: masked
+    ind[5::23] = 1 << 30
+    w.indices = ind
+    start, end = int(w.indptr[1]), int(w.indptr[2])
+    w.indices[start:end] = -1  # an all-masked row
+    pool, view = build_gpu_pool(w)
+    out, lse = run_gpu(w, view)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, range(6), "masked-dup")
+
+
+def test_strided_q_and_out_with_sentinel_columns():
+    say("fwd strided q and out views")
+    w = small_workload(700, 3, 8, 500, [100, 150, 70])
+    pool, view = build_gpu_pool(w)
+    qbig = torch.zeros((3, 8, 640), dtype=torch.bfloat16, device=DEV)
+    qbig[:, :, 32:608] = w.q.to(DEV)
+    q = qbig[:, :, 32:608]
+    outbig = torch.full((3, 8, 600), 1234.0, dtype=torch.bfloat16, device=DEV)
+    out_view = outbig[:, :, 40:600]
+    out, lse = mla.sparse_fwd(q, view, w.indptr.to(DEV), w.indices.to(DEV), w.softmax_scale, out=out_view,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == out_view.data_ptr()
+    assert torch.all(outbig[:, :, :40] == 1234.0) and torch.all(outbig[:, :, 552:] == 1234.0)
+    check_rows(w, pool, outbig[:, :, 40:552], lse, range(3), "strided")
+
+
+def test_raw_records_pow2_and_arbitrary_scales():
+    """Records not made by the writer: every finite code, per-tile scales that
+    are powers of two (the FlyDSL slice's precondition) or arbitrary floats.
+    Scales are kept to the range a writer gives unit-variance latents
+    (|value| <= 448 * 2^-4).  With values up to 448 * 2^7, random-sign
+    queries make sum |q_d k_d| ~1e3 times the logit itself, so float32
+    accumulation alone moves logits by ~1e-3 and the +-1e3-sized V terms
+    turn that into output errors the absolute part of the bar does not
+    allow; that is a property of any float32-accumulating contraction, not
+    of this kernel."""
+    say("fwd raw records")
+    rng = np.random.default_rng(800)
+    n_rec = 700
+    codes = rng.integers(0, 256, (n_rec, 512), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00  # no NaN codes
+    scales = np.where(rng.random((n_rec, 4)) < 0.5, 2.0 ** rng.integers(-12, -3, (n_rec, 4)),
+                      np.exp(rng.normal(-5.5, 0.7, (n_rec, 4)))).astype("<f4")
+    rope = torch.randn((n_rec, 64), generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    rec = np.zeros((n_rec, 656), np.uint8)
+    rec[:, :512] = codes
+    rec[:, 512:528] = scales.view(np.uint8).reshape(n_rec, 16)
+    rec[:, 528:] = bf16_bits(rope).view(np.uint8).reshape(n_rec, 128)
+    q = torch.randn((4, 16, 576), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    indptr = np.array([0, 300, 301, 301, 700])
+    ind = rng.permutation(n_rec)[:700].astype(np.int32)
+    # A softmax scale that gives these keys logits of standard deviation ~3
+    # (the spread of the long-context workload): the 2e-3 LSE bar is an
+    # absolute one, met by float32 accumulation at realistic logit sizes.
+    keys, _ = decode_records(rec)
+    qf = q.float().numpy().astype(np.float64)
+    scale = float(3.0 / np.std(qf[0] @ keys.T))
+    out, lse = mla.sparse_fwd(q.to(DEV), torch.from_numpy(rec).to(DEV), torch.from_numpy(indptr.astype(np.int32)).to(DEV),
+                              torch.from_numpy(ind).to(DEV), scale, return_lse=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, indptr, ind, scale)
+    assert_fwd_close(out, lse, ref_out, ref_lse, "raw-records")
+
+
+def test_no_indices_and_no_tokens():
+    say("fwd nnz=0 and T=0")
+    kv = torch.zeros((10, 656), dtype=torch.uint8, device=DEV)
+    q = torch.randn((3, 4, 576), device=DEV).to(torch.bfloat16)
+    indptr = torch.zeros(4, dtype=torch.int32, device=DEV)
+    indices = torch.zeros(0, dtype=torch.int32, device=DEV)
+    out = torch.full((3, 4, 512), 5.0, dtype=torch.bfloat16, device=DEV)
+    out, lse = mla.sparse_fwd(q, kv, indptr, indices, 1.0, out=out, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    q0 = torch.zeros((0, 4, 576), dtype=torch.bfloat16, device=DEV)
+    out0, lse0 = mla.sparse_fwd(q0, kv, torch.zeros(1, dtype=torch.int32, device=DEV), indices, 1.0,
+                                return_lse=True)
+    assert out0.shape == (0, 4, 512) and lse0.shape == (0, 4)
+
+
+def test_binding_rejects_unsupported_calls():
+    kv = torch.zeros((4, 656), dtype=torch.uint8, device=DEV)
+    ip = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    ix = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):  # 17 heads
+        mla.sparse_fwd(torch.zeros((1, 17, 576), dtype=torch.bfloat16, device=DEV), kv, ip, ix, 1.0)
+    with pytest.raises(ValueError):  # fp16 query
+        mla.sparse_fwd(torch.zeros((1, 2, 576), dtype=torch.float16, device=DEV), kv, ip, ix, 1.0)
+    with pytest.raises(ValueError):  # padded page pitch
+        pages = torch.zeros(2 * 70 * 656, dtype=torch.uint8, device=DEV).view(2, 70, 656)[:, :64]
+        mla.sparse_fwd(torch.zeros((1, 2, 576), dtype=torch.bfloat16, device=DEV), pages, ip, ix, 1.0)
+    with pytest.raises(ValueError):  # out narrower than 512
+        mla.sparse_fwd(torch.zeros((1, 2, 576), dtype=torch.bfloat16, device=DEV), kv, ip, ix, 1.0,
+                       out=torch.zeros((1, 2, 256), dtype=torch.bfloat16, device=DEV))
