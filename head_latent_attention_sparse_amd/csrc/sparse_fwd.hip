@@ -36,8 +36,13 @@ namespace {
 constexpr int kTileKeys = 64;
 constexpr int kThreads = 256;
 constexpr int kChunks = kRecordBytes / 16;                                // 41 x 16 B per record
-constexpr int kTileChunks = kTileKeys * kChunks;                          // 2624
-constexpr int kChunksPerThread = (kTileChunks + kThreads - 1) / kThreads;  // 11
+constexpr int kChunksPerThread = (kChunks + 3) / 4;                       // 11 (4 threads per record)
+static_assert(kThreads == 4 * kTileKeys, "gather mapping: 4 threads per record");
+static_assert(4 * (kChunksPerThread - 1) + 1 == kChunks, "the last chunk belongs to sub 0 alone");
+// Softmax weights may grow to 2^kLazyRescale before the running reference
+// (and with it O and the sum) is moved up.
+constexpr float kLazyRescale = 8.0f;
+constexpr int MLA_MAX_SPLITS_DEVICE = 1024;  // the C ABI's MLA_MAX_SPLITS
 constexpr int kLogitPitch = kTileKeys + 4;                                 // floats per head row
 
 typedef __attribute__((address_space(3))) intx2_t lds_intx2_t;
@@ -136,28 +141,31 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Gather mapping: 4 threads per record; thread (rec, sub) moves the 16-byte
+  // chunks sub, sub + 4, ..., so one slot lookup serves all its loads and
+  // every load / store sits at a constant offset from one address.  A
+  // masked or past-the-end key is not loaded: its LDS row keeps whatever
+  // finite chunks the registers held (zero at first), which is harmless
+  // because its logit is -inf and its softmax weight exactly 0.
+  const int grec = tid >> 2;
+  const int gsub = tid & 3;
   u32x4_t pf[kChunksPerThread];
-  auto issue_gather = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c < kTileChunks) {
-        const int r = c / kChunks;
-        const int piece = c - r * kChunks;
-        const int slot = s_slot[buf][r];
-        if (slot >= 0)
-          v = *reinterpret_cast<const u32x4_t *>(p.rec + (int64_t)slot * kRecordBytes + piece * 16);
-      }
-      pf[i] = v;
+  for (int i = 0; i < kChunksPerThread; ++i) pf[i] = u32x4_t{0u, 0u, 0u, 0u};
+  auto issue_gather = [&](int buf) {
+    const int slot = s_slot[buf][grec];
+    if (slot >= 0) {
+      const uint8_t *src = p.rec + (int64_t)slot * kRecordBytes + 16 * gsub;
+#pragma unroll
+      for (int i = 0; i < kChunksPerThread - 1; ++i) pf[i] = *reinterpret_cast<const u32x4_t *>(src + 64 * i);
+      if (gsub == 0) pf[kChunksPerThread - 1] = *reinterpret_cast<const u32x4_t *>(src + 64 * (kChunksPerThread - 1));
     }
   };
   auto store_gather = [&]() {
+    uint8_t *dst = s_rec + grec * kRecordBytes + 16 * gsub;
 #pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < kTileChunks) *reinterpret_cast<u32x4_t *>(s_rec + c * 16) = pf[i];
-    }
+    for (int i = 0; i < kChunksPerThread - 1; ++i) *reinterpret_cast<u32x4_t *>(dst + 64 * i) = pf[i];
+    if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
   };
 
   auto compute_tile = [&](int buf) {
@@ -213,19 +221,23 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
     mt = fmaxf(mt, xor_shuffle(mt, 16));
     mt = fmaxf(mt, xor_shuffle(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
-    float psum = 0.f;
+    // Lazy rescale: the reference m_run only moves when the tile max passes
+    // it by more than kLazyRescale (weights stay <= 2^kLazyRescale), so O
+    // and the sum are rescaled rarely; any reference gives the same result.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
+      m_run = m_new;
+    }
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sv[i] = fast_exp2(sv[i] - m_ref);
-      psum += sv[i];
+      l_run += sv[i];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
 
     // ---- P^T operands (B: column = head n, k-slot j = key 32ks + 8g + j),
     // each weight times its key's scale for latent tile `wave`.
@@ -313,41 +325,74 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   }
 }
 
-// Combine split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s.
-// One workgroup per (row, 4 heads); each thread owns 8 columns of one head.
-template <bool kLse>
-__global__ __launch_bounds__(256) void merge_kernel(const float *ws_out, const float *ws_lse, int32_t splits,
-                                                    int32_t heads, uint16_t *out, int64_t o_st, int64_t o_sh,
-                                                    float *lse) {
-  const int head_groups = (heads + 3) >> 2;
-  const int64_t t = blockIdx.x / head_groups;
-  const int h = (blockIdx.x - (int)(t * head_groups)) * 4 + (threadIdx.x >> 6);
-  const int col = (threadIdx.x & 63) * 8;
-  if (h >= heads) return;
-  const float *lp = ws_lse + t * splits * heads + h;
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lp[(int64_t)s * heads]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float w = fast_exp2(lp[(int64_t)s * heads] - mx);
-      tot += w;
-      const float *o = ws_out + ((t * splits + s) * heads + h) * kLatent + col;
-      const floatx4_t a = *reinterpret_cast<const floatx4_t *>(o);
-      const floatx4_t b = *reinterpret_cast<const floatx4_t *>(o + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] += w * a[j];
-        acc[4 + j] += w * b[j];
-      }
-    }
+// Combine split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s
+// (an empty partial, lse_s = -inf, weighs 0; all empty -> out 0, lse -inf).
+// One workgroup per (row, head, 128-column quarter): the split weights are
+// computed once into LDS, then 8 split lanes x 32 column quads accumulate and
+// reduce through LDS, so a row with many splits reads its partials with
+// 256 threads in parallel.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeSplitLanes = 8;
+
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
+  for (int m = 1; m < 64; m <<= 1) {
+    const float o = xor_shuffle(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // red may still be read by a previous reduction
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) v = is_max ? fmaxf(v, red[w]) : v + red[w];
+  return v;
+}
+
+template <bool kLse>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse, int32_t splits,
+                                                              int32_t heads, uint16_t *out, int64_t o_st, int64_t o_sh,
+                                                              float *lse) {
+  __shared__ float s_w[MLA_MAX_SPLITS_DEVICE];
+  __shared__ floatx4_t s_part[kMergeSplitLanes][32];
+  __shared__ float s_red[kMergeThreads / 64];
+  const int tid = threadIdx.x;
+  const int quarter = blockIdx.x & 3;
+  const int64_t th = blockIdx.x >> 2;  // t * heads + h
+  const int64_t t = th / heads;
+  const int h = (int)(th - t * heads);
+  const float *lp = ws_lse + t * splits * heads + h;  // split s at lp[s * heads]
+
+  float mx = -INFINITY;
+  for (int s = tid; s < splits; s += kMergeThreads) mx = fmaxf(mx, lp[(int64_t)s * heads]);
+  mx = block_reduce(mx, s_red, true);
+  float tot = 0.f;
+  for (int s = tid; s < splits; s += kMergeThreads) {
+    const float w = mx == -INFINITY ? 0.f : fast_exp2(lp[(int64_t)s * heads] - mx);
+    s_w[s] = w;
+    tot += w;
+  }
+  tot = block_reduce(tot, s_red, false);  // its barriers also publish s_w
+
+  const int sl = tid >> 5;  // split lane
+  const int cq = tid & 31;  // column quad
+  const int col = quarter * 128 + 4 * cq;
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = sl; s < splits; s += kMergeSplitLanes) {
+    const float w = s_w[s];
+    const floatx4_t o = *reinterpret_cast<const floatx4_t *>(ws_out + ((t * splits + s) * heads + h) * kLatent + col);
+    acc += o * w;
+  }
+  s_part[sl][cq] = acc;
+  __syncthreads();
+  if (sl == 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dst[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-  if (kLse && col == 0) lse[t * heads + h] = mx == -INFINITY ? -INFINITY : (mx + fast_log2(tot)) * kLn2;
+    for (int k = 1; k < kMergeSplitLanes; ++k) acc += s_part[k][cq];
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
+    dst[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    dst[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    if (kLse && quarter == 0 && cq == 0) lse[t * heads + h] = mx == -INFINITY ? -INFINITY : (mx + fast_log2(tot)) * kLn2;
+  }
 }
 
 template <typename IdxT>
@@ -383,12 +428,12 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   sparse_fwd_kernel<IdxT, true, false><<<grid, block, 0, stream>>>(k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 mgrid((unsigned)((int64_t)a.num_tokens * ((a.num_heads + 3) / 4)));
+  const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * 4));
   if (lse)
-    merge_kernel<true><<<mgrid, 256, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
+    merge_kernel<true><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
                                                   a.out_stride_token, a.out_stride_head, a.lse);
   else
-    merge_kernel<false><<<mgrid, 256, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
+    merge_kernel<false><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
                                                    a.out_stride_token, a.out_stride_head, nullptr);
   return hipGetLastError();
 }
