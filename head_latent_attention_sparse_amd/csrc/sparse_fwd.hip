@@ -65,6 +65,22 @@ struct FwdKernelArgs {
   float *ws_lse;
 };
 
+// QK^T partial of latent tile B for this lane's key: sum over the tile's 128
+// dims of (q_hi * 2^-k + q_lo * 2^-(k+k2)) * code, in float32; the key's
+// tile scale is applied by the caller.  Both operands use the MFMA's
+// hardware k order within the tile (k = 64 * (byte / 16) + 16 * g + byte % 16).
+template <int B>
+__device__ __forceinline__ floatx4_t qk_latent_tile(const uint8_t *krec, int g, const intx8_t (&qa)[4][2],
+                                                   const uint32_t (&qscale)[2]) {
+  const u32x4_t c0 = *reinterpret_cast<const u32x4_t *>(krec + 128 * B + 16 * g);
+  const u32x4_t c1 = *reinterpret_cast<const u32x4_t *>(krec + 128 * B + 64 + 16 * g);
+  const intx8_t codes = {(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  acc = mfma_16x16x128_e4m3<B>(qa[B][0], codes, acc, qscale[0]);
+  acc = mfma_16x16x128_e4m3<B>(qa[B][1], codes, acc, qscale[1]);
+  return acc;
+}
+
 template <typename IdxT, bool kSplit, bool kLse>
 __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_rec[kTileKeys * kRecordBytes];
@@ -109,30 +125,111 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     return v;
   };
 
-  // ---- query fragments (MFMA A operand: row = head n, 8 k-slots per lane).
-  // Pair P < 8 covers latent d = 128*(P/2) + 64*(P%2) + 16*g + [0, 16);
-  // pair 8 covers rope d = 512 + 16*g + [0, 16).  Step 0 of a pair takes
-  // the first 8 of those 16 dims, step 1 the last 8; the record bytes are
-  // read with the same mapping, so the contraction covers every d once.
-  u32x4_t qf[9][2];
+  // ---- query, rope part: bf16 MFMA A operand (row = head n); lane (n, g)
+  // k-slots j of step st <-> rope d = 16g + 8st + j; the record's rope bytes
+  // are read with the same mapping.
+  u32x4_t qr[2];
   {
     const uint32_t *qrow = reinterpret_cast<const uint32_t *>(p.q + t * p.q_st + (int64_t)n * p.q_sh);
 #pragma unroll
-    for (int P = 0; P < 9; ++P) {
-      const int d0 = P < 8 ? 128 * (P >> 1) + 64 * (P & 1) + 16 * g : 512 + 16 * g;
+    for (int st = 0; st < 2; ++st) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (n < p.heads) {
+        const uint32_t *src = qrow + ((kLatent + 16 * g + 8 * st) >> 1);
+        v.x = src[0];
+        v.y = src[1];
+        v.z = src[2];
+        v.w = src[3];
+      }
+      qr[st] = v;
+    }
+  }
+
+  // ---- query, latent part: two E4M3 terms per 32-element group, so that
+  // QK^T runs on the records' E4M3 codes directly (scaled fp8 MFMA, no code
+  // conversion).  For the 32 values x of (head h, latent tile blk, k-block
+  // kb), with amax = max |x|:
+  //   y  = x * 2^k,  k = 7 - floor(log2 amax)         (amax * 2^k in [128, 256))
+  //   hi = y with its mantissa cut to 3 bits if |y| >= 2^-6, else 0 (exact E4M3)
+  //   r  = y - hi (exact);  lo = E4M3(r * 2^k2),  k2 = 7 - floor(log2 max |r|)
+  // so x = hi * 2^-k + lo * 2^-(k+k2): exact when r * 2^k2 is an E4M3 normal,
+  // otherwise off by at most 2^-12 * 2^-k (about 2^-19 of amax).  The two
+  // powers of two are the e8m0 block scales of the A operand.  Staged through
+  // the tile buffer before its first use: wave w splits latent tile w, lane
+  // (h, kb) = (n, g) one group; then every wave reads all four tiles.
+  intx8_t qa[4][2];     // [latent tile][hi, lo], MFMA A layout
+  uint32_t qscale[2];   // [hi, lo]: byte blk = e8m0 scale of (head n, k-block g) in tile blk
+  {
+    uint8_t *q_lds = s_rec;                     // [(blk * 2 + part) * 16 + h][128] codes
+    uint8_t *sc_lds = s_rec + 4 * 2 * 16 * 128;  // [(part * 16 + h) * 4 + kb] words, byte blk
+    float x[32];
+    {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q + t * p.q_st + (int64_t)n * p.q_sh +
+                                                               128 * wave + 32 * g);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (n < p.heads) {
-          const uint32_t *src = qrow + ((d0 + 8 * st) >> 1);
-          v.x = src[0];
-          v.y = src[1];
-          v.z = src[2];
-          v.w = src[3];
-        }
-        qf[P][st] = v;
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t w2 = n < p.heads ? src[e] : 0u;
+        x[2 * e] = as_float(w2 << 16);
+        x[2 * e + 1] = as_float(w2 & 0xFFFF0000u);
       }
     }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hw[i] = lw[i] = 0u;
+    uint32_t e_hi = 127u, e_lo = 127u;
+    if (amax > 0.f) {
+      const int k = min(7 - ((int)(as_u32(amax) >> 23) - 127), 126);
+      const float pk = as_float((uint32_t)(127 + k) << 23);
+      float hv[32];
+      float rmax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float y = x[e] * pk;
+        hv[e] = fabsf(y) >= 0x1p-6f ? as_float(as_u32(y) & 0xFFF00000u) : 0.f;
+        x[e] = y - hv[e];
+        rmax = fmaxf(rmax, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        hw[i] = pack_e4m3x2<true>(hv[4 * i + 2], hv[4 * i + 3], pack_e4m3x2<false>(hv[4 * i], hv[4 * i + 1], 0u));
+      e_hi = (uint32_t)(127 - k);
+      if (rmax > 0.f) {
+        // k2 >= 0 always (|r| < 256); the cap keeps the lo scale byte >= 1.
+        const int k2 = min(7 - ((int)(as_u32(rmax) >> 23) - 127), 126 - k);
+        const float pk2 = as_float((uint32_t)(127 + k2) << 23);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          lw[i] = pack_e4m3x2<true>(x[4 * i + 2] * pk2, x[4 * i + 3] * pk2,
+                                    pack_e4m3x2<false>(x[4 * i] * pk2, x[4 * i + 1] * pk2, 0u));
+        e_lo = (uint32_t)(127 - k - k2);
+      }
+    }
+    uint8_t *hrow = q_lds + ((wave * 2 + 0) * 16 + n) * 128 + 32 * g;
+    uint8_t *lrow = q_lds + ((wave * 2 + 1) * 16 + n) * 128 + 32 * g;
+    *reinterpret_cast<u32x4_t *>(hrow) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4_t *>(hrow + 16) = u32x4_t{hw[4], hw[5], hw[6], hw[7]};
+    *reinterpret_cast<u32x4_t *>(lrow) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    *reinterpret_cast<u32x4_t *>(lrow + 16) = u32x4_t{lw[4], lw[5], lw[6], lw[7]};
+    sc_lds[((0 * 16 + n) * 4 + g) * 4 + wave] = (uint8_t)e_hi;
+    sc_lds[((1 * 16 + n) * 4 + g) * 4 + wave] = (uint8_t)e_lo;
+    __syncthreads();
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const uint8_t *row = q_lds + ((blk * 2 + part) * 16 + n) * 128;
+        const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(row + 16 * g);
+        const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(row + 64 + 16 * g);
+        qa[blk][part] = intx8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      }
+    }
+    qscale[0] = *reinterpret_cast<const uint32_t *>(sc_lds + ((0 * 16 + n) * 4 + g) * 4);
+    qscale[1] = *reinterpret_cast<const uint32_t *>(sc_lds + ((1 * 16 + n) * 4 + g) * 4);
+    __syncthreads();  // the tile buffer is overwritten by the first gather
   }
 
   float m_run = -INFINITY;  // running max of head n's logits (exp2 domain)
@@ -147,7 +244,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // masked or past-the-end key is not loaded: its LDS row keeps whatever
   // finite chunks the registers held (zero at first), which is harmless
   // because its logit is -inf and its softmax weight exactly 0.
-  const int grec = tid >> 2;
+  // Records r, r+4, r+8, r+12 share a 16-lane group: at a 164-dword pitch
+  // they start 16 banks apart, so each 16-lane LDS store pass is conflict-free.
+  const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
   const int gsub = tid & 3;
   u32x4_t pf[kChunksPerThread];
 #pragma unroll
@@ -172,25 +271,16 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     // ---- QK^T for keys 16*wave + n
     const uint8_t *krec = s_rec + (wave * 16 + n) * kRecordBytes;
     const u32x4_t scv = *reinterpret_cast<const u32x4_t *>(krec + kScaleOffset);
-    floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ph = 0; ph < 2; ++ph) {
-        const u32x4_t c = *reinterpret_cast<const u32x4_t *>(krec + 128 * b + 64 * ph + 16 * g);
-        acc = mfma_16x16x32_bf16(as_bf16x8(qf[2 * b + ph][0]), e4m3x8_to_bf16x8(c.x, c.y), acc);
-        acc = mfma_16x16x32_bf16(as_bf16x8(qf[2 * b + ph][1]), e4m3x8_to_bf16x8(c.z, c.w), acc);
-      }
-      const float sc = as_float(scv[b]);
-      sacc += acc * sc;
-    }
+    floatx4_t sacc = qk_latent_tile<0>(krec, g, qa, qscale) * as_float(scv[0]);
+    sacc += qk_latent_tile<1>(krec, g, qa, qscale) * as_float(scv[1]);
+    sacc += qk_latent_tile<2>(krec, g, qa, qscale) * as_float(scv[2]);
+    sacc += qk_latent_tile<3>(krec, g, qa, qscale) * as_float(scv[3]);
     {
       const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g);
       const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g + 16);
       floatx4_t racc = {0.f, 0.f, 0.f, 0.f};
-      racc = mfma_16x16x32_bf16(as_bf16x8(qf[8][0]), as_bf16x8(r0), racc);
-      racc = mfma_16x16x32_bf16(as_bf16x8(qf[8][1]), as_bf16x8(r1), racc);
+      racc = mfma_16x16x32_bf16(as_bf16x8(qr[0]), as_bf16x8(r0), racc);
+      racc = mfma_16x16x32_bf16(as_bf16x8(qr[1]), as_bf16x8(r1), racc);
       sacc += racc;
     }
     const bool valid = s_slot[buf][wave * 16 + n] >= 0;
