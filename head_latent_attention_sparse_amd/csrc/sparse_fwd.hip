@@ -113,17 +113,58 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   }
   const int ntiles = (int)((end - beg + kTileKeys - 1) / kTileKeys);
 
-  // Slot of entry `tid` of tile `tile`, or -1 (masked, past the end, or
-  // outside the pool).
-  auto fetch_slot = [&](int tile) -> int {
+  // Slot of entry j of tile `tile`, or -1 (masked, past the end, or outside
+  // the pool).
+  auto fetch_entry = [&](int tile, int j) -> int {
     int v = -1;
-    const int64_t e = beg + (int64_t)tile * kTileKeys + tid;
+    const int64_t e = beg + (int64_t)tile * kTileKeys + j;
     if (tile < ntiles && e < end) {
       const int64_t x = (int64_t)indices[e];
       if (x >= 0 && x < p.num_records) v = (int)x;
     }
     return v;
   };
+  auto fetch_slot = [&](int tile) -> int { return fetch_entry(tile, tid); };
+
+  // Gather mapping: 4 threads per record; thread (rec, sub) moves the 16-byte
+  // chunks sub, sub + 4, ..., so one slot lookup serves all its loads and
+  // every load / store sits at a constant offset from one address.  A
+  // masked or past-the-end key is not loaded: its LDS row keeps whatever
+  // finite chunks the registers held (zero at first), which is harmless
+  // because its logit is -inf and its softmax weight exactly 0.
+  // Records r, r+4, r+8, r+12 share a 16-lane group: at a 164-dword pitch
+  // they start 16 banks apart, so each 16-lane LDS store pass is conflict-free.
+  const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
+  const int gsub = tid & 3;
+  u32x4_t pf[kChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kChunksPerThread; ++i) pf[i] = u32x4_t{0u, 0u, 0u, 0u};
+  auto issue_gather_slot = [&](int slot) {
+    if (slot >= 0) {
+      const uint8_t *src = p.rec + (int64_t)slot * kRecordBytes + 16 * gsub;
+#pragma unroll
+      for (int i = 0; i < kChunksPerThread - 1; ++i) pf[i] = *reinterpret_cast<const u32x4_t *>(src + 64 * i);
+      if (gsub == 0) pf[kChunksPerThread - 1] = *reinterpret_cast<const u32x4_t *>(src + 64 * (kChunksPerThread - 1));
+    }
+  };
+  auto issue_gather = [&](int buf) { issue_gather_slot(s_slot[buf][grec]); };
+  auto store_gather = [&]() {
+    uint8_t *dst = s_rec + grec * kRecordBytes + 16 * gsub;
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread - 1; ++i) *reinterpret_cast<u32x4_t *>(dst + 64 * i) = pf[i];
+    if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
+  };
+
+  // ---- start the first tile early: the slots of tiles 0 and 1 (for the
+  // masks) and this thread's record of tile 0 are requested before the
+  // query, and tile 0's gather is issued before the query split is computed,
+  // so these round trips overlap instead of following one another.
+  int slot_t0 = -1, slot_t1 = -1;
+  if (tid < kTileKeys) {
+    slot_t0 = fetch_slot(0);
+    slot_t1 = fetch_slot(1);
+  }
+  const int my_slot0 = fetch_entry(0, grec);
 
   // ---- query, rope part: bf16 MFMA A operand (row = head n); lane (n, g)
   // k-slots j of step st <-> rope d = 16g + 8st + j; the record's rope bytes
@@ -173,6 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
         x[2 * e + 1] = as_float(w2 & 0xFFFF0000u);
       }
     }
+    issue_gather_slot(my_slot0);  // tile 0, in flight during the split
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -237,35 +279,6 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   floatx4_t oacc[8];        // O^T[128*wave + 16*mt + 4*g + j][head n]
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) oacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Gather mapping: 4 threads per record; thread (rec, sub) moves the 16-byte
-  // chunks sub, sub + 4, ..., so one slot lookup serves all its loads and
-  // every load / store sits at a constant offset from one address.  A
-  // masked or past-the-end key is not loaded: its LDS row keeps whatever
-  // finite chunks the registers held (zero at first), which is harmless
-  // because its logit is -inf and its softmax weight exactly 0.
-  // Records r, r+4, r+8, r+12 share a 16-lane group: at a 164-dword pitch
-  // they start 16 banks apart, so each 16-lane LDS store pass is conflict-free.
-  const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
-  const int gsub = tid & 3;
-  u32x4_t pf[kChunksPerThread];
-#pragma unroll
-  for (int i = 0; i < kChunksPerThread; ++i) pf[i] = u32x4_t{0u, 0u, 0u, 0u};
-  auto issue_gather = [&](int buf) {
-    const int slot = s_slot[buf][grec];
-    if (slot >= 0) {
-      const uint8_t *src = p.rec + (int64_t)slot * kRecordBytes + 16 * gsub;
-#pragma unroll
-      for (int i = 0; i < kChunksPerThread - 1; ++i) pf[i] = *reinterpret_cast<const u32x4_t *>(src + 64 * i);
-      if (gsub == 0) pf[kChunksPerThread - 1] = *reinterpret_cast<const u32x4_t *>(src + 64 * (kChunksPerThread - 1));
-    }
-  };
-  auto store_gather = [&]() {
-    uint8_t *dst = s_rec + grec * kRecordBytes + 16 * gsub;
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread - 1; ++i) *reinterpret_cast<u32x4_t *>(dst + 64 * i) = pf[i];
-    if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
-  };
 
   auto compute_tile = [&](int buf) {
     // ---- QK^T for keys 16*wave + n
@@ -361,16 +374,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   if (ntiles > 0) {
     int next_slot = -1;
     if (tid < kTileKeys) {
-      s_slot[0][tid] = fetch_slot(0);
-      next_slot = fetch_slot(1);
-    }
-    __syncthreads();
-    issue_gather(0);
-    store_gather();
-    if (tid < kTileKeys) {
-      s_slot[1][tid] = next_slot;
+      s_slot[0][tid] = slot_t0;
+      s_slot[1][tid] = slot_t1;
       next_slot = fetch_slot(2);
     }
+    store_gather();  // tile 0 (issued before the query split)
     __syncthreads();
     if (ntiles > 1) issue_gather(1);
     for (int k = 0; k < ntiles; ++k) {
