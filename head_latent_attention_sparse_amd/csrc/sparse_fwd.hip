@@ -113,18 +113,22 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   }
   const int ntiles = (int)((end - beg + kTileKeys - 1) / kTileKeys);
 
-  // Slot of entry j of tile `tile`, or -1 (masked, past the end, or outside
-  // the pool).
-  auto fetch_entry = [&](int tile, int j) -> int {
-    int v = -1;
+  // Raw id of entry j of tile `tile`.  The load is unconditional (an entry
+  // past the end reads element 0 instead, which exists: with no indices the
+  // array is a placeholder that points at indptr) and its value is not looked
+  // at here, so it stays in flight until slot_of turns it into a slot, an
+  // iteration later for the index prefetch.
+  auto fetch_entry = [&](int tile, int j) -> IdxT {
     const int64_t e = beg + (int64_t)tile * kTileKeys + j;
-    if (tile < ntiles && e < end) {
-      const int64_t x = (int64_t)indices[e];
-      if (x >= 0 && x < p.num_records) v = (int)x;
-    }
-    return v;
+    return indices[e < end ? e : 0];
   };
-  auto fetch_slot = [&](int tile) -> int { return fetch_entry(tile, tid); };
+  // The slot entry j of tile `tile` names, or -1 (past the end, masked, or
+  // outside the pool).
+  auto slot_of = [&](IdxT raw, int tile, int j) -> int {
+    const int64_t x = (int64_t)raw;
+    const bool in_range = beg + (int64_t)tile * kTileKeys + j < end;
+    return (in_range && x >= 0 && x < p.num_records) ? (int)x : -1;
+  };
 
   // Gather mapping: 4 threads per record; thread (rec, sub) moves the 16-byte
   // chunks sub, sub + 4, ..., so one slot lookup serves all its loads and
@@ -159,12 +163,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // masks) and this thread's record of tile 0 are requested before the
   // query, and tile 0's gather is issued before the query split is computed,
   // so these round trips overlap instead of following one another.
-  int slot_t0 = -1, slot_t1 = -1;
-  if (tid < kTileKeys) {
-    slot_t0 = fetch_slot(0);
-    slot_t1 = fetch_slot(1);
-  }
-  const int my_slot0 = fetch_entry(0, grec);
+  const IdxT slot_t0 = fetch_entry(0, lane);
+  const IdxT slot_t1 = fetch_entry(1, lane);
+  const IdxT my_id0 = fetch_entry(0, grec);
 
   // ---- query, rope part: bf16 MFMA A operand (row = head n); lane (n, g)
   // k-slots j of step st <-> rope d = 16g + 8st + j; the record's rope bytes
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
         x[2 * e + 1] = as_float(w2 & 0xFFFF0000u);
       }
     }
-    issue_gather_slot(my_slot0);  // tile 0, in flight during the split
+    issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0, in flight during the split
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
@@ -372,11 +373,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   };
 
   if (ntiles > 0) {
-    int next_slot = -1;
+    IdxT next_slot = fetch_entry(2, lane);
     if (tid < kTileKeys) {
-      s_slot[0][tid] = slot_t0;
-      s_slot[1][tid] = slot_t1;
-      next_slot = fetch_slot(2);
+      s_slot[0][tid] = slot_of(slot_t0, 0, tid);
+      s_slot[1][tid] = slot_of(slot_t1, 1, tid);
     }
     store_gather();  // tile 0 (issued before the query split)
     __syncthreads();
@@ -387,10 +387,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       __syncthreads();
       if (k + 1 < ntiles) {
         store_gather();  // tile k + 1
-        if (tid < kTileKeys) {
-          s_slot[buf][tid] = next_slot;  // tile k + 2
-          next_slot = fetch_slot(k + 3);
-        }
+        if (tid < kTileKeys) s_slot[buf][tid] = slot_of(next_slot, k + 2, tid);  // tile k + 2
+        next_slot = fetch_entry(k + 3, lane);
         __syncthreads();
         if (k + 2 < ntiles) issue_gather(buf);
       }
