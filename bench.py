@@ -87,7 +87,7 @@ def main():
     indptr, indices = w.indptr.to(dev), w.indices.to(dev)
     out = torch.empty((t_count, heads, 512), dtype=torch.bfloat16, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    splits = mla.num_splits(t_count, nnz, cus)
+    split_wgs = mla.split_workgroups(t_count, nnz, cus)
     ws_bytes = mla.lib().mla_sparse_fwd_workspace_size(t_count, heads, nnz, 0, 0)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -164,7 +164,7 @@ def main():
             "records": w.num_records,
             "csr_entries": nnz,
             "valid_entries": nnz_valid,
-            "splits": splits,
+            "split_kv_workgroups": split_wgs,
             "parallelism": "single GPU",
         },
         "gathered_record_GBps": gathered / (ms_per_step * 1e-3) / 1e9,

@@ -10,12 +10,12 @@ from .ops import (  # noqa: F401
     FLAG_RETURN_LSE,
     KV_LORA_RANK,
     MAX_HEADS,
-    MAX_SPLITS,
+    MAX_CHUNK_TILES,
     QK_ROPE_HEAD_DIM,
     RECORD_BYTES,
     MlaError,
     cache_insert,
     lib,
-    num_splits,
+    split_workgroups,
     sparse_fwd,
 )

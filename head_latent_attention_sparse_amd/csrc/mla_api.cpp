@@ -85,26 +85,32 @@ mla_status_t workspace_get(int device, size_t bytes, void **out) {
 }
 
 constexpr uint32_t kKnownFlags =
-    MLA_FLAG_HAS_INVALID | MLA_FLAG_RETURN_LSE | MLA_FLAG_INDEX_I64 | MLA_FLAG_SPLITS_MASK;
+    MLA_FLAG_HAS_INVALID | MLA_FLAG_RETURN_LSE | MLA_FLAG_INDEX_I64 | MLA_FLAG_CHUNK_MASK;
 
-// Entries per split below which splitting a row further does not pay: eight
-// 64-key tiles.
-constexpr int64_t kMinEntriesPerSplit = 512;
+// Smallest chunk the plan kernel picks on its own: eight 64-key tiles (the
+// device side uses the same value).
+constexpr int64_t kMinChunkEntries = 512;
 
-int32_t plan_splits(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags) {
-  const uint32_t forced = (flags & MLA_FLAG_SPLITS_MASK) >> 16;
-  if (forced) return forced > MLA_MAX_SPLITS ? MLA_MAX_SPLITS : (int32_t)forced;
-  if (tokens <= 0 || cus <= 0) return 1;
-  // Aim for two resident workgroups per compute unit over the whole launch,
-  // but never split a row's average share below kMinEntriesPerSplit.
+// Split-KV plan from host values only (never index values): 0 = one
+// workgroup per row; otherwise the number of workgroups of the partial pass,
+// an upper bound on the chunks.  Split when the rows alone cannot give two
+// workgroups per compute unit and the average row is longer than a minimum
+// chunk; the plan kernel then sizes the chunks on the device so they fit
+// those 2 x CU workgroups in one round.  A forced chunk size (flags) gives
+// the bound ceil(nnz / chunk) + T.
+int64_t plan_split(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags, int32_t *forced_chunk) {
+  const uint32_t forced = (flags & MLA_FLAG_CHUNK_MASK) >> 16;
+  *forced_chunk = 0;
+  if (tokens <= 0) return 0;
+  if (forced) {
+    *forced_chunk = (int32_t)(forced * 64);
+    return mla::forced_chunk_bound(tokens, nnz, *forced_chunk);
+  }
+  if (cus <= 0) return 0;
   const int64_t target = 2 * (int64_t)cus;
-  if (tokens >= target) return 1;
-  int64_t s = (target + tokens - 1) / tokens;
-  const int64_t by_len = (nnz / tokens) / kMinEntriesPerSplit;
-  if (s > by_len) s = by_len;
-  if (s < 1) s = 1;
-  if (s > MLA_MAX_SPLITS) s = MLA_MAX_SPLITS;
-  return (int32_t)s;
+  if (tokens >= target || tokens > mla::kMaxSplitRows) return 0;
+  if ((nnz + tokens - 1) / tokens <= kMinChunkEntries) return 0;
+  return target;
 }
 
 }  // namespace
@@ -126,9 +132,10 @@ const char *mla_status_string(mla_status_t st) {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 
-int32_t mla_sparse_fwd_num_splits(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags) {
-  if (num_tokens < 0 || num_indices < 0 || num_cus < 0 || (flags & ~kKnownFlags)) return 0;
-  return plan_splits(num_tokens, num_indices, num_cus, flags);
+int64_t mla_sparse_fwd_split_workgroups(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags) {
+  if (num_tokens < 0 || num_indices < 0 || num_cus < 0 || (flags & ~kKnownFlags)) return -1;
+  int32_t forced = 0;
+  return plan_split(num_tokens, num_indices, num_cus, flags, &forced);
 }
 
 size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_indices, uint32_t flags,
@@ -137,16 +144,18 @@ size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int6
     fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd_workspace_size: invalid arguments");
     return (size_t)-1;
   }
-  const uint32_t forced = (flags & MLA_FLAG_SPLITS_MASK) >> 16;
   int cus = 0;
-  if (!forced) {
+  if (!(flags & MLA_FLAG_CHUNK_MASK)) {
     cus = device_cus(device);
     if (cus <= 0) {
       fail(MLA_ERR_HIP, "mla_sparse_fwd_workspace_size: cannot query device %d", device);
       return (size_t)-1;
     }
   }
-  return mla::split_workspace_bytes(num_tokens, num_heads, plan_splits(num_tokens, num_indices, cus, flags));
+  int32_t forced = 0;
+  const int64_t bound = plan_split(num_tokens, num_indices, cus, flags, &forced);
+  if (bound <= 0) return 0;
+  return mla::split_layout(num_tokens, num_heads, bound).bytes;
 }
 
 mla_status_t mla_workspace_reserve(int device, size_t bytes) {
@@ -192,6 +201,9 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
   if (!aligned(kv_indptr, idx_align) || !aligned(kv_indices, idx_align))
     return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: index arrays not aligned to their element size");
   if (want_lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: lse not 4-byte aligned");
+  if ((flags & MLA_FLAG_CHUNK_MASK) && num_tokens > mla::kMaxSplitRows)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: forced split-KV serves at most %lld rows",
+                (long long)mla::kMaxSplitRows);
   if (num_tokens == 0) return MLA_OK;
   if (!q || !out || !kv_indptr) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL q, out or kv_indptr");
   if (want_lse && !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: MLA_FLAG_RETURN_LSE with lse == NULL");
@@ -200,12 +212,14 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
 
   int device = -1;
   if (hipGetDevice(&device) != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: hipGetDevice failed");
-  const int32_t forced = (int32_t)((flags & MLA_FLAG_SPLITS_MASK) >> 16);
+  const bool forced = (flags & MLA_FLAG_CHUNK_MASK) != 0;
   const int cus = forced ? 0 : device_cus(device);
   if (!forced && cus <= 0) return fail(MLA_ERR_HIP, "mla_sparse_fwd: cannot query device %d", device);
-  const int32_t splits = plan_splits(num_tokens, num_indices, cus, flags);
-  if ((int64_t)num_tokens * splits > INT32_MAX)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: %lld rows x %d splits exceeds the grid", (long long)num_tokens, splits);
+  int32_t forced_chunk = 0;
+  const int64_t bound = plan_split(num_tokens, num_indices, cus, flags, &forced_chunk);
+
+  if (bound > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: %lld chunks exceed the grid", (long long)bound);
 
   mla::FwdArgs a;
   a.q = static_cast<const uint16_t *>(q);
@@ -214,7 +228,7 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
   a.records = static_cast<const uint8_t *>(kv_records);
   a.num_records = num_records;
   a.indptr = kv_indptr;
-  a.indices = num_indices > 0 ? kv_indices : kv_indptr;  // never read when empty
+  a.indices = num_indices > 0 ? kv_indices : kv_indptr;  // element 0 may be read, never used
   a.num_indices = num_indices;
   a.index_i64 = i64;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -224,23 +238,26 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
   a.out_stride_token = out_stride_token;
   a.out_stride_head = out_stride_head;
   a.lse = want_lse ? lse : nullptr;
-  a.splits = splits;
+  a.chunk_forced = forced_chunk;
+  a.chunk_bound = bound;
   a.ws_out = nullptr;
   a.ws_lse = nullptr;
-  if (splits > 1) {
-    const size_t need = mla::split_workspace_bytes(num_tokens, num_heads, splits);
+  a.ws_prefix = nullptr;
+  if (bound > 0) {
+    const mla::SplitLayout l = mla::split_layout(num_tokens, num_heads, bound);
     void *ws = workspace;
     if (ws) {
-      if (workspace_bytes < need)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+      if (workspace_bytes < l.bytes)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.bytes);
       if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace not 256-byte aligned");
     } else {
-      mla_status_t st = workspace_get(device, need, &ws);
+      mla_status_t st = workspace_get(device, l.bytes, &ws);
       if (st != MLA_OK) return st;
     }
-    a.ws_out = static_cast<float *>(ws);
-    a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                         mla::split_workspace_lse_offset(num_tokens, num_heads, splits));
+    char *base = static_cast<char *>(ws);
+    a.ws_out = reinterpret_cast<float *>(base + l.out_off);
+    a.ws_lse = reinterpret_cast<float *>(base + l.lse_off);
+    a.ws_prefix = reinterpret_cast<int32_t *>(base + l.prefix_off);
   }
   hipError_t e = mla::launch_sparse_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: launch failed: %s", hipGetErrorString(e));

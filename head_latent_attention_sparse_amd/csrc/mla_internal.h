@@ -21,9 +21,15 @@ struct FwdArgs {
   uint16_t *out;
   int64_t out_stride_token, out_stride_head;  // elements
   float *lse;                                 // [T, H] or nullptr
-  int32_t splits;
-  float *ws_out;  // [T, splits, H, 512] float32 when splits > 1
-  float *ws_lse;  // [T, splits, H] float32 (base-2 log-sum-exp) when splits > 1
+  // Split-KV: chunk_bound == 0 = one workgroup per row.  Otherwise rows are
+  // cut into chunks of chunk_forced entries if > 0, else of a size the
+  // partial pass picks on the device so the chunks fit chunk_bound, its grid
+  // (an upper bound on the number of chunks).  At most 512 rows.
+  int32_t chunk_forced;
+  int64_t chunk_bound;
+  float *ws_out;       // [chunk_bound, H, 512] float32 partials
+  float *ws_lse;       // [chunk_bound, H] float32 base-2 log-sum-exp
+  int32_t *ws_prefix;  // [T + 1] first chunk of each row
 };
 
 hipError_t launch_sparse_fwd(const FwdArgs &a, hipStream_t stream);
@@ -41,17 +47,27 @@ struct InsertArgs {
 
 hipError_t launch_cache_insert(const InsertArgs &a, hipStream_t stream);
 
-// Bytes of split partials for a call (0 when splits <= 1), 256-byte aligned parts.
-inline size_t split_workspace_bytes(int64_t tokens, int32_t heads, int32_t splits) {
-  if (splits <= 1 || tokens <= 0) return 0;
-  const size_t rows = (size_t)tokens * (size_t)splits * (size_t)heads;
-  const size_t out_bytes = (rows * 512 * sizeof(float) + 255) & ~(size_t)255;
-  const size_t lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
-  return out_bytes + lse_bytes;
+// Workspace of a chunked (split-KV) call, in 256-byte aligned parts:
+// partials, partial LSEs, row prefix.
+struct SplitLayout {
+  size_t out_off, lse_off, prefix_off, bytes;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline SplitLayout split_layout(int64_t tokens, int32_t heads, int64_t chunk_bound) {
+  SplitLayout l;
+  const size_t rows = (size_t)chunk_bound * (size_t)heads;
+  l.out_off = 0;
+  l.lse_off = align256(rows * 512 * sizeof(float));
+  l.prefix_off = l.lse_off + align256(rows * sizeof(float));
+  l.bytes = l.prefix_off + align256(((size_t)tokens + 1) * sizeof(int32_t));
+  return l;
 }
-inline size_t split_workspace_lse_offset(int64_t tokens, int32_t heads, int32_t splits) {
-  const size_t rows = (size_t)tokens * (size_t)splits * (size_t)heads;
-  return (rows * 512 * sizeof(float) + 255) & ~(size_t)255;
+// Upper bound on the number of chunks of a forced chunk size: every row adds
+// at most one partial chunk.
+inline int64_t forced_chunk_bound(int64_t tokens, int64_t nnz, int32_t chunk_entries) {
+  return (nnz + chunk_entries - 1) / chunk_entries + tokens;
 }
+
+constexpr int64_t kMaxSplitRows = 512;  // rows the split pass serves
 
 }  // namespace mla

@@ -42,7 +42,6 @@ static_assert(4 * (kChunksPerThread - 1) + 1 == kChunks, "the last chunk belongs
 // Softmax weights may grow to 2^kLazyRescale before the running reference
 // (and with it O and the sum) is moved up.
 constexpr float kLazyRescale = 8.0f;
-constexpr int MLA_MAX_SPLITS_DEVICE = 1024;  // the C ABI's MLA_MAX_SPLITS
 constexpr int kLogitPitch = kTileKeys + 4;                                 // floats per head row
 
 typedef __attribute__((address_space(3))) intx2_t lds_intx2_t;
@@ -57,13 +56,160 @@ struct FwdKernelArgs {
   int64_t nnz;
   float scale_log2;
   int32_t heads;
-  int32_t splits;
   uint16_t *out;
   int64_t o_st, o_sh;
   float *lse;
   float *ws_out;
   float *ws_lse;
+  int32_t *ws_prefix;
+  int32_t tokens;
+  int32_t forced_chunk;  // split pass: chunk size if > 0, else chosen by split_plan
+  int64_t bound;         // split pass: its workgroups, an upper bound on the chunks
 };
+
+// ---- Split-KV plan, computed by every workgroup of the partial pass ----
+// The same plan in every workgroup (and no separate launch): row lengths
+// with the forward's clamping of indptr; a chunk size; each row's first
+// chunk (an exclusive prefix); then this workgroup's chunk.  The chunk size
+// is `forced` if given, otherwise the smallest of kPlanCandidates multiples
+// of 64 (at least kMinChunk) whose chunk total fits the `bound` workgroups,
+// so the partial pass is one round of the shortest chunks.  The candidates
+// run from ceil(n / bound) to ceil(n / (bound - rows)) (n = sum of lengths,
+// rows = the non-empty ones); the last always fits, since
+// sum ceil(len / C) <= n / C + rows.  Prefix values are capped at `bound`:
+// a non-monotone indptr (overlapping rows) loses chunks instead of indexing
+// out of range.  Thread i owns rows 2i and 2i + 1.
+constexpr int kMaxSplitRows = 512;
+constexpr int64_t kMinChunk = 512;
+constexpr int kPlanCandidates = 4;
+static_assert(kMaxSplitRows == 2 * kThreads, "split plan: two rows per thread");
+
+// ceil(len / c) for 0 <= len < 2^29 and 64 <= c < 2^30: a float estimate
+// (off by at most 2) and an exact integer correction.
+__device__ __forceinline__ int32_t ceil_div_rcp(int32_t len, int32_t c, float rcp) {
+  int32_t q = (int32_t)((float)len * rcp);
+  int32_t r = len - q * c;
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (r < 0) {
+      q -= 1;
+      r += c;
+    }
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (r >= c) {
+      q += 1;
+      r -= c;
+    }
+  return q + (r > 0 ? 1 : 0);
+}
+
+struct SplitPlanLds {
+  unsigned long long n;
+  int32_t rows;
+  int32_t cnt[kPlanCandidates];
+  int32_t wave_tot[4];
+  int32_t hit[3];  // row, begin, end of this workgroup's chunk
+};
+
+template <typename IdxT>
+__device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t, int64_t &beg, int64_t &end) {
+  SplitPlanLds &sh = *reinterpret_cast<SplitPlanLds *>(scratch);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
+  const int32_t tokens = p.tokens;
+  const int32_t r0 = 2 * tid;
+
+  int32_t len[2] = {0, 0}, rb[2] = {0, 0};
+  if (r0 < tokens) {
+    const int64_t x0 = (int64_t)indptr[r0], x1 = (int64_t)indptr[r0 + 1];
+    const int64_t x2 = r0 + 1 < tokens ? (int64_t)indptr[r0 + 2] : x1;
+    const int64_t xs[3] = {x0, x1, x2};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int64_t b = xs[i], e = xs[i + 1];
+      b = b < 0 ? 0 : (b > p.nnz ? p.nnz : b);
+      e = e < b ? b : (e > p.nnz ? p.nnz : e);
+      rb[i] = (int32_t)b;  // nnz < 2^29
+      len[i] = (int32_t)(e - b);
+    }
+    if (r0 + 1 >= tokens) len[1] = 0;
+  }
+  if (tid == 0) {
+    sh.n = 0;
+    sh.rows = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanCandidates; ++k) sh.cnt[k] = 0;
+  }
+  __syncthreads();
+
+  int32_t chunk = p.forced_chunk;
+  if (chunk <= 0) {
+    if (len[0] + len[1] > 0) {
+      atomicAdd(&sh.n, (unsigned long long)(len[0] + len[1]));
+      atomicAdd(&sh.rows, (len[0] > 0) + (len[1] > 0));
+    }
+    __syncthreads();
+    const int64_t n = (int64_t)sh.n, rows = sh.rows, bound = p.bound;
+    const int64_t lo = max(kMinChunk, ((n + bound - 1) / bound + 63) & ~(int64_t)63);
+    const int64_t slack = bound > rows ? bound - rows : 1;
+    const int64_t hi = min(max(lo, ((n + slack - 1) / slack + 63) & ~(int64_t)63), (int64_t)1 << 29);
+    const int64_t step = max((int64_t)64, ((hi - lo) / (kPlanCandidates - 1) + 63) & ~(int64_t)63);
+#pragma unroll
+    for (int k = 0; k < kPlanCandidates; ++k) {
+      const int32_t c = (int32_t)min(lo + step * k, hi);
+      const float rcp = 1.0f / (float)c;
+      const int32_t cnt = ceil_div_rcp(len[0], c, rcp) + ceil_div_rcp(len[1], c, rcp);
+      if (cnt) atomicAdd(&sh.cnt[k], cnt);
+    }
+    __syncthreads();
+    chunk = (int32_t)hi;  // always fits
+#pragma unroll
+    for (int k = kPlanCandidates - 1; k >= 0; --k)
+      if (sh.cnt[k] <= bound) chunk = (int32_t)min(lo + step * k, hi);
+  }
+
+  // first chunk of each row: one block scan of this thread's two counts
+  const float rcp = 1.0f / (float)chunk;
+  const int32_t c0 = ceil_div_rcp(len[0], chunk, rcp), c1 = ceil_div_rcp(len[1], chunk, rcp);
+  int32_t incl = c0 + c1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) sh.wave_tot[wave] = incl;
+  __syncthreads();
+  int64_t first0 = incl - c0 - c1;
+  for (int w = 0; w < wave; ++w) first0 += sh.wave_tot[w];
+  const int64_t cap = p.bound;
+  const int64_t total = min((int64_t)sh.wave_tot[0] + sh.wave_tot[1] + sh.wave_tot[2] + sh.wave_tot[3], cap);
+  const int64_t f0 = min(first0, cap), f1 = min(first0 + c0, cap), f2 = min(first0 + c0 + c1, cap);
+  if (blockIdx.x == 0) {  // the merge reads the prefix
+    if (r0 < tokens) p.ws_prefix[r0] = (int32_t)f0;
+    if (r0 + 1 < tokens) p.ws_prefix[r0 + 1] = (int32_t)f1;
+    if (tid == 0) p.ws_prefix[tokens] = (int32_t)total;
+  }
+  const int64_t b = blockIdx.x;
+  if (r0 < tokens && f0 <= b && b < f1) {
+    sh.hit[0] = r0;
+    sh.hit[1] = rb[0] + (int32_t)(b - f0) * chunk;
+    sh.hit[2] = rb[0] + len[0];
+  } else if (r0 + 1 < tokens && f1 <= b && b < f2) {
+    sh.hit[0] = r0 + 1;
+    sh.hit[1] = rb[1] + (int32_t)(b - f1) * chunk;
+    sh.hit[2] = rb[1] + len[1];
+  }
+  __syncthreads();
+  const bool has_work = b < total;
+  if (has_work) {
+    t = sh.hit[0];
+    beg = sh.hit[1];
+    end = beg + chunk < sh.hit[2] ? beg + chunk : (int64_t)sh.hit[2];
+  }
+  __syncthreads();  // the scratch (the tile buffer) is reused next
+  return has_work;
+}
 
 // QK^T partial of latent tile B for this lane's key: sum over the tile's 128
 // dims of (q_hi * 2^-k + q_lo * 2^-(k+k2)) * code, in float32; the key's
@@ -94,22 +240,20 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   const int n = lane & 15;  // MFMA row/column index of this lane
   const int g = lane >> 4;  // MFMA k-group of this lane
 
-  const int64_t t = blockIdx.x / p.splits;
-  const int split = blockIdx.x - (int)(t * p.splits);
-
-  // ---- this workgroup's share of the row's CSR entries
-  const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
+  // ---- this workgroup's CSR entries: a whole row, or a chunk of one
   const IdxT *indices = static_cast<const IdxT *>(p.indices);
-  int64_t rb = (int64_t)indptr[t];
-  int64_t re = (int64_t)indptr[t + 1];
-  rb = rb < 0 ? 0 : (rb > p.nnz ? p.nnz : rb);
-  re = re < rb ? rb : (re > p.nnz ? p.nnz : re);
-  int64_t beg = rb, end = re;
+  int64_t t, beg, end;
   if (kSplit) {
-    const int64_t per = (((re - rb) + p.splits - 1) / p.splits + kTileKeys - 1) & ~(int64_t)(kTileKeys - 1);
-    beg = rb + per * split;
-    beg = beg > re ? re : beg;
-    end = beg + per > re ? re : beg + per;
+    if (!split_plan<IdxT>(p, s_rec, t, beg, end)) return;  // whole workgroup
+  } else {
+    const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
+    t = blockIdx.x;
+    int64_t rb = (int64_t)indptr[t];
+    int64_t re = (int64_t)indptr[t + 1];
+    rb = rb < 0 ? 0 : (rb > p.nnz ? p.nnz : rb);
+    re = re < rb ? rb : (re > p.nnz ? p.nnz : re);
+    beg = rb;
+    end = re;
   }
   const int ntiles = (int)((end - beg + kTileKeys - 1) / kTileKeys);
 
@@ -412,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       if (kLse && wave == 0 && g == 0)
         p.lse[t * p.heads + n] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
     } else {
-      const int64_t row = (t * p.splits + split) * p.heads + n;
+      const int64_t row = (int64_t)blockIdx.x * p.heads + n;  // chunk id * H + head
       float *wo = p.ws_out + row * kLatent + 128 * wave + 4 * g;
 #pragma unroll
       for (int m = 0; m < 8; ++m) *reinterpret_cast<floatx4_t *>(wo + 16 * m) = oacc[m] * inv;
@@ -421,14 +565,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   }
 }
 
-// Combine split partials: lse = log2 sum_s 2^lse_s, out = sum_s 2^(lse_s - lse) o_s
-// (an empty partial, lse_s = -inf, weighs 0; all empty -> out 0, lse -inf).
-// One workgroup per (row, head, 128-column quarter): the split weights are
-// computed once into LDS, then 8 split lanes x 32 column quads accumulate and
-// reduce through LDS, so a row with many splits reads its partials with
-// 256 threads in parallel.
+// Combine a row's chunk partials: lse = log2 sum_s 2^lse_s,
+// out = sum_s 2^(lse_s - lse) o_s (an empty partial, lse_s = -inf, weighs 0;
+// no partial or all empty -> out 0, lse -inf).  One workgroup per (row,
+// head, 128-column quarter): 8 chunk lanes x 32 column quads accumulate and
+// reduce through LDS, so a row with many chunks is read by 256 threads.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeSplitLanes = 8;
+constexpr int kMergeChunkLanes = 8;
 
 __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
   for (int m = 1; m < 64; m <<= 1) {
@@ -445,44 +588,44 @@ __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) 
 }
 
 template <bool kLse>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse, int32_t splits,
-                                                              int32_t heads, uint16_t *out, int64_t o_st, int64_t o_sh,
-                                                              float *lse) {
-  __shared__ float s_w[MLA_MAX_SPLITS_DEVICE];
-  __shared__ floatx4_t s_part[kMergeSplitLanes][32];
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse,
+                                                              const int32_t *prefix, int32_t heads, uint16_t *out,
+                                                              int64_t o_st, int64_t o_sh, float *lse) {
+  __shared__ floatx4_t s_part[kMergeChunkLanes][32];
   __shared__ float s_red[kMergeThreads / 64];
   const int tid = threadIdx.x;
   const int quarter = blockIdx.x & 3;
   const int64_t th = blockIdx.x >> 2;  // t * heads + h
   const int64_t t = th / heads;
   const int h = (int)(th - t * heads);
-  const float *lp = ws_lse + t * splits * heads + h;  // split s at lp[s * heads]
+  const int64_t c0 = prefix[t];
+  const int nc = prefix[t + 1] - (int)c0;
+  const float *lp = ws_lse + c0 * heads + h;  // chunk s at lp[s * heads]
 
   float mx = -INFINITY;
-  for (int s = tid; s < splits; s += kMergeThreads) mx = fmaxf(mx, lp[(int64_t)s * heads]);
+  for (int s = tid; s < nc; s += kMergeThreads) mx = fmaxf(mx, lp[(int64_t)s * heads]);
   mx = block_reduce(mx, s_red, true);
   float tot = 0.f;
-  for (int s = tid; s < splits; s += kMergeThreads) {
-    const float w = mx == -INFINITY ? 0.f : fast_exp2(lp[(int64_t)s * heads] - mx);
-    s_w[s] = w;
-    tot += w;
-  }
-  tot = block_reduce(tot, s_red, false);  // its barriers also publish s_w
+  if (mx != -INFINITY)
+    for (int s = tid; s < nc; s += kMergeThreads) tot += fast_exp2(lp[(int64_t)s * heads] - mx);
+  tot = block_reduce(tot, s_red, false);
 
-  const int sl = tid >> 5;  // split lane
+  const int cl = tid >> 5;  // chunk lane
   const int cq = tid & 31;  // column quad
   const int col = quarter * 128 + 4 * cq;
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = sl; s < splits; s += kMergeSplitLanes) {
-    const float w = s_w[s];
-    const floatx4_t o = *reinterpret_cast<const floatx4_t *>(ws_out + ((t * splits + s) * heads + h) * kLatent + col);
-    acc += o * w;
+  if (mx != -INFINITY) {
+    for (int s = cl; s < nc; s += kMergeChunkLanes) {
+      const float w = fast_exp2(lp[(int64_t)s * heads] - mx);
+      const floatx4_t o = *reinterpret_cast<const floatx4_t *>(ws_out + ((c0 + s) * heads + h) * kLatent + col);
+      acc += o * w;
+    }
   }
-  s_part[sl][cq] = acc;
+  s_part[cl][cq] = acc;
   __syncthreads();
-  if (sl == 0) {
+  if (cl == 0) {
 #pragma unroll
-    for (int k = 1; k < kMergeSplitLanes; ++k) acc += s_part[k][cq];
+    for (int k = 1; k < kMergeChunkLanes; ++k) acc += s_part[k][cq];
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
     dst[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -504,33 +647,37 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   k.nnz = a.num_indices;
   k.scale_log2 = a.scale_log2;
   k.heads = a.num_heads;
-  k.splits = a.splits;
   k.out = a.out;
   k.o_st = a.out_stride_token;
   k.o_sh = a.out_stride_head;
   k.lse = a.lse;
   k.ws_out = a.ws_out;
   k.ws_lse = a.ws_lse;
+  k.ws_prefix = a.ws_prefix;
+  k.tokens = a.num_tokens;
+  k.forced_chunk = a.chunk_forced;
+  k.bound = a.chunk_bound;
   const dim3 block(kThreads);
-  const dim3 grid((unsigned)((int64_t)a.num_tokens * a.splits));
   const bool lse = a.lse != nullptr;
-  if (a.splits <= 1) {
+  if (a.chunk_bound <= 0) {
+    const dim3 grid((unsigned)a.num_tokens);
     if (lse)
       sparse_fwd_kernel<IdxT, false, true><<<grid, block, 0, stream>>>(k);
     else
       sparse_fwd_kernel<IdxT, false, false><<<grid, block, 0, stream>>>(k);
     return hipGetLastError();
   }
-  sparse_fwd_kernel<IdxT, true, false><<<grid, block, 0, stream>>>(k);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  sparse_fwd_kernel<IdxT, true, false><<<dim3((unsigned)a.chunk_bound), block, 0, stream>>>(k);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * 4));
   if (lse)
-    merge_kernel<true><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
-                                                  a.out_stride_token, a.out_stride_head, a.lse);
+    merge_kernel<true><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
+                                                           a.out_stride_token, a.out_stride_head, a.lse);
   else
-    merge_kernel<false><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.splits, a.num_heads, a.out,
-                                                   a.out_stride_token, a.out_stride_head, nullptr);
+    merge_kernel<false><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
+                                                            a.out_stride_token, a.out_stride_head, nullptr);
   return hipGetLastError();
 }
 

@@ -23,12 +23,12 @@ RECORD_BYTES = 656
 KV_LORA_RANK = 512
 QK_ROPE_HEAD_DIM = 64
 MAX_HEADS = 16
-MAX_SPLITS = 1024
+MAX_CHUNK_TILES = 65535
 
 FLAG_HAS_INVALID = 1 << 0
 FLAG_RETURN_LSE = 1 << 1
 FLAG_INDEX_I64 = 1 << 2
-SPLITS_SHIFT = 16
+CHUNK_SHIFT = 16
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_HIP",
           4: "MLA_ERR_OUT_OF_MEMORY"}
@@ -39,7 +39,7 @@ _I64, _I32, _U32, _F32, _P, _SZ = (ctypes.c_int64, ctypes.c_int32, ctypes.c_uint
 SIGNATURES = {
     "mla_sparse_fwd": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P, _I64, _I64,
                               _P, _P, _SZ, _P]),
-    "mla_sparse_fwd_num_splits": (_I32, [_I64, _I64, _I32, _U32]),
+    "mla_sparse_fwd_split_workgroups": (_I64, [_I64, _I64, _I32, _U32]),
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
@@ -114,19 +114,22 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def num_splits(num_tokens, num_indices, num_cus, forced=0):
-    """The split-KV count the library picks (host only)."""
-    return lib().mla_sparse_fwd_num_splits(num_tokens, num_indices, num_cus, forced << SPLITS_SHIFT)
+def split_workgroups(num_tokens, num_indices, num_cus, chunk_tiles=0):
+    """The split-KV plan (host only): 0 = one workgroup per row, else the
+    workgroups of the partial pass; ``chunk_tiles`` forces chunks of that
+    many 64-key tiles."""
+    return lib().mla_sparse_fwd_split_workgroups(num_tokens, num_indices, num_cus, chunk_tiles << CHUNK_SHIFT)
 
 
 def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid=False, out=None,
-               return_lse=False, num_splits=0, workspace=None):
+               return_lse=False, chunk_tiles=0, workspace=None):
     """Sparse MLA forward over fp8_ds_mla records -> (out, lse or None).
 
     q [T, H, 576] bf16 (H <= 16, stride(2) == 1); kv_cache a record pool
     view; kv_indptr [T + 1] and kv_indices [nnz] int32 or int64 (the same
-    dtype, contiguous); out optional [T, H, >= 512] bf16.  ``num_splits``
-    forces the split-KV count (0 = the library's choice).  ``workspace``
+    dtype, contiguous); out optional [T, H, >= 512] bf16.  ``chunk_tiles``
+    forces split-KV with chunks of that many 64-key tiles (0 = the library's
+    plan).  ``workspace``
     optionally supplies the split partial buffer (a CUDA uint8 tensor).
     """
     if not (torch.is_tensor(q) and q.is_cuda and q.ndim == 3 and q.dtype == torch.bfloat16):
@@ -159,9 +162,9 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
     flags = (FLAG_HAS_INVALID if has_invalid else 0) | (FLAG_RETURN_LSE if return_lse else 0)
     if kv_indices.dtype == torch.int64:
         flags |= FLAG_INDEX_I64
-    if not 0 <= num_splits <= MAX_SPLITS:
-        raise ValueError(f"num_splits must be in 0 .. {MAX_SPLITS}")
-    flags |= num_splits << SPLITS_SHIFT
+    if not 0 <= chunk_tiles <= MAX_CHUNK_TILES:
+        raise ValueError(f"chunk_tiles must be in 0 .. {MAX_CHUNK_TILES}")
+    flags |= chunk_tiles << CHUNK_SHIFT
     L = lib()
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
     with torch.cuda.device(dev):

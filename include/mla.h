@@ -48,15 +48,16 @@ typedef enum mla_status {
 #define MLA_QK_DIM 576
 #define MLA_MAX_HEADS 16
 #define MLA_MAX_INDICES (1 << 29) /* num_indices must be below this */
-#define MLA_MAX_SPLITS 1024
 
 /* mla_sparse_fwd flags */
 #define MLA_FLAG_HAS_INVALID (1u << 0) /* negative slot ids may occur (they are masked either way) */
 #define MLA_FLAG_RETURN_LSE (1u << 1)  /* write lse */
 #define MLA_FLAG_INDEX_I64 (1u << 2)   /* kv_indptr and kv_indices are int64 (default int32) */
-/* Force the split-KV count to n (1 .. MLA_MAX_SPLITS); 0 = chosen by the library. */
-#define MLA_FLAG_SPLITS(n) (((uint32_t)(n)) << 16)
-#define MLA_FLAG_SPLITS_MASK (0xFFFFu << 16)
+/* Force split-KV with chunks of n 64-key tiles (1 .. 65535); 0 = the
+ * library's plan (mla_sparse_fwd_split_workgroups).  Split-KV serves at most
+ * 512 rows: a forced split with more is MLA_ERR_UNSUPPORTED. */
+#define MLA_FLAG_CHUNK_TILES(n) (((uint32_t)(n)) << 16)
+#define MLA_FLAG_CHUNK_MASK (0xFFFFu << 16)
 
 /*
  * mla_sparse_fwd - sparse attention of absorbed MLA queries over records.
@@ -71,10 +72,12 @@ typedef enum mla_status {
  *     out[t,h,:] = sum_j softmax(z)_j v_j      (bf16, round to nearest even),
  *     lse[t,h]   = ln sum_j exp(z_j)           (float32, natural log).
  * A row with no such entry gives out = 0 and lse = -inf.  A slot listed
- * twice counts twice.  Rows of many keys are split over several workgroups
- * (split-KV) whose float32 partials are combined by their LSEs in a second
- * launch, the merge named by merge_attn_states on the kimi_k3 nvidia mla
- * page.
+ * twice counts twice.  When there are too few rows to fill the GPU (and at
+ * most 512), each row's entries are cut into fixed-size chunks (split-KV):
+ * every workgroup of a partial pass plans the chunks from indptr on the
+ * device and computes one chunk's float32 partial and LSE, and a second
+ * launch combines each row's partials by their LSEs (the merge named by
+ * merge_attn_states on the kimi_k3 nvidia mla page).
  *
  *  q            bf16 [num_tokens, num_heads, 576], element (t,h,d) at
  *               q + t*q_stride_token + h*q_stride_head + d (strides in
@@ -97,7 +100,7 @@ typedef enum mla_status {
  *               base 4-byte aligned.
  *  lse          float32 [T, num_heads] contiguous; required with
  *               MLA_FLAG_RETURN_LSE, ignored otherwise.
- *  workspace    scratch for split-KV partials of at least
+ *  workspace    scratch for the split-KV plan and partials of at least
  *               mla_sparse_fwd_workspace_size(...) bytes, 256-byte aligned,
  *               or NULL: the library then uses a buffer it owns per device
  *               (allocated on first need, grown when too small; growing
@@ -116,15 +119,18 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * mla_sparse_fwd_num_splits - the split-KV count mla_sparse_fwd uses (host
- * only, no device access).  It depends on T, num_indices, the device's
- * compute-unit count and the forced count in flags, never on index values:
- * the count is fixed by a bound known on the host, as the split counts of
- * the decode cores on the kimi_k3 specialized-decode page are
- * (PreparedMla.fill_splits / max_seq).  Returns 0 for invalid arguments.
+ * mla_sparse_fwd_split_workgroups - the split-KV plan mla_sparse_fwd uses
+ * (host only, no device access): 0 = one workgroup per row; otherwise the
+ * number of workgroups of the partial pass, an upper bound on the number of
+ * chunks.  It depends on T, num_indices, the device's compute-unit count and
+ * the forced chunk in flags, never on index values: the launch is fixed from
+ * bounds known on the host, as the split counts of the decode cores on the
+ * kimi_k3 specialized-decode page are (PreparedMla.fill_splits / max_seq).
+ * Without a forced chunk the chunk size is then picked on the device from
+ * the actual row lengths: the smallest multiple of 64 entries (at least 512)
+ * whose chunks fit that many workgroups.  Returns -1 for invalid arguments.
  */
-int32_t mla_sparse_fwd_num_splits(int64_t num_tokens, int64_t num_indices, int32_t num_cus,
-                                  uint32_t flags);
+int64_t mla_sparse_fwd_split_workgroups(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags);
 
 /*
  * mla_sparse_fwd_workspace_size - bytes of split-KV workspace a call with
@@ -179,7 +185,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

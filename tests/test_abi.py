@@ -83,6 +83,7 @@ def fwd(**kw):
     (dict(out=None), INVALID),
     (dict(indptr=None), INVALID),
     (dict(indices=None), INVALID),
+    (dict(T=513, flags=2 | (4 << 16)), UNSUPPORTED),  # forced split-KV: at most 512 rows
 ])
 def test_fwd_rejections(kw, status):
     st, msg = fwd(**kw)
@@ -128,29 +129,32 @@ def test_insert_zero_tokens_is_a_no_op():
 
 
 @pytest.mark.parametrize("tokens,nnz,cus,forced,want", [
-    (4096, 4096 * 2048, 256, 0, 1),     # sparse prefill: enough rows
-    (1024, 1024 * 1024, 256, 0, 1),     # insert + attend
-    (4, 512, 256, 0, 1),                # tiny rows: no split
-    (8, 8 * 131072, 256, 0, 64),        # long context: 512 workgroups
-    (64, 64 * 4608, 256, 0, 8),         # paged decode
-    (8, 8 * 131072, 256, 7, 7),         # forced
-    (8, 100, 256, 5000, 1024),          # forced, clamped
-    (0, 0, 256, 0, 1),
+    (4096, 4096 * 2048, 256, 0, 0),     # sparse prefill: enough rows, no split
+    (1024, 1024 * 1024, 256, 0, 0),     # insert + attend
+    (4, 512, 256, 0, 0),                # tiny rows fit one chunk
+    (8, 8 * 131072, 256, 0, 512),       # long context: one round of 2 x CUs
+    (64, 294912, 256, 0, 512),          # paged decode
+    (8, 100, 256, 0, 0),
+    (8, 8 * 131072, 256, 7, 2341 + 8),  # forced 7 tiles: ceil(nnz / 448) + T
+    (4096, 100, 256, 1, 2 + 4096),      # forced even with many rows
+    (0, 0, 256, 0, 0),
 ])
 def test_split_plan(tokens, nnz, cus, forced, want):
-    assert mla.num_splits(tokens, nnz, cus, forced) == want
+    assert mla.split_workgroups(tokens, nnz, cus, forced) == want
 
 
 def test_split_plan_depends_only_on_host_values():
     lib = mla.lib()
-    assert lib.mla_sparse_fwd_num_splits(-1, 0, 256, 0) == 0
-    assert lib.mla_sparse_fwd_num_splits(8, 0, 256, 1 << 5) == 0  # unknown flag bit
+    assert lib.mla_sparse_fwd_split_workgroups(-1, 0, 256, 0) == -1
+    assert lib.mla_sparse_fwd_split_workgroups(8, 0, 256, 1 << 5) == -1  # unknown flag bit
 
 
-def test_workspace_size_of_forced_split_needs_no_device():
+def test_workspace_size_of_forced_chunks_needs_no_device():
     lib = mla.lib()
-    size = lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 4 << 16, 0)
-    rows = 8 * 4 * 16
-    assert size == ((rows * 512 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
-    assert lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 1 << 16, 0) == 0
+    a256 = lambda x: (x + 255) // 256 * 256
+    # 4-tile (256-entry) chunks: at most ceil(1000 / 256) + 8 = 12 chunks
+    bound = 4 + 8
+    want = a256(bound * 16 * 512 * 4) + a256(bound * 16 * 4) + a256(9 * 4)
+    assert lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 4 << 16, 0) == want
+    assert lib.mla_sparse_fwd_workspace_size(0, 16, 0, 4 << 16, 0) == 0
     assert lib.mla_sparse_fwd_workspace_size(8, 17, 1000, 4 << 16, 0) == ctypes.c_size_t(-1).value

@@ -123,7 +123,7 @@ def test_config3_sparse_prefill_full_sampled():
 def test_config4_long_context_reduced():
     say("fwd config4 reduced (T=3, N=20000): automatic split-KV")
     w = workloads.long_context(tokens=3, records=20000)
-    assert mla.num_splits(3, w.nnz, torch.cuda.get_device_properties(0).multi_processor_count) > 1
+    assert mla.split_workgroups(3, w.nnz, torch.cuda.get_device_properties(0).multi_processor_count) > 0
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
     check_rows(w, pool, out, lse, range(3), "config4-reduced")
@@ -197,13 +197,29 @@ def test_warmup_problem(golden_dir):
             assert torch.all(lse == fx["expected_lse"])
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 64])
-def test_forced_splits(splits):
-    say(f"fwd forced splits={splits}")
-    w = small_workload(400, 4, 16, 3000, [2500, 700, 64, 0], p_invalid=0.1, latent_std=2.0)
+@pytest.mark.parametrize("chunk_tiles", [1, 2, 7, 64])
+def test_forced_chunks(chunk_tiles):
+    """Split-KV with forced chunk sizes: rows of 2500, 700, 64, 0 and 130
+    entries give 1..40 chunks per row, an empty row and a single partial."""
+    say(f"fwd forced chunk_tiles={chunk_tiles}")
+    w = small_workload(400, 5, 16, 3000, [2500, 700, 64, 0, 130], p_invalid=0.1, latent_std=2.0)
     pool, view = build_gpu_pool(w)
-    out, lse = run_gpu(w, view, num_splits=splits)
-    check_rows(w, pool, out, lse, range(4), f"splits={splits}")
+    out, lse = run_gpu(w, view, chunk_tiles=chunk_tiles)
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, range(5), f"chunk_tiles={chunk_tiles}")
+
+
+def test_forced_chunks_all_masked_row_and_int64():
+    say("fwd forced chunks: all-masked row spanning chunks, int64 indices")
+    w = small_workload(410, 3, 8, 900, [300, 500, 200], p_invalid=0.3)
+    start, end = int(w.indptr[1]), int(w.indptr[2])
+    w.indices[start:end] = -1
+    pool, view = build_gpu_pool(w)
+    out, lse = mla.sparse_fwd(w.q.to(DEV), view, w.indptr.to(torch.int64).to(DEV), w.indices.to(torch.int64).to(DEV),
+                              w.softmax_scale, return_lse=True, chunk_tiles=2)
+    torch.cuda.synchronize()
+    check_all_rows_sane(w, out, lse)
+    check_rows(w, pool, out, lse, range(3), "chunks-i64")
 
 
 def test_ragged_lengths_int32_and_int64():
