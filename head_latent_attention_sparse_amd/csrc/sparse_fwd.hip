@@ -7,26 +7,32 @@
 // slot list, keys k = [latent | rope] (576), values v = latent (512),
 // negative slots masked, an empty row giving out 0 and lse -inf.
 //
-// Design (one workgroup of 4 waves per (row, split), 64-key tiles):
+// Design (one workgroup of 4 waves per row, or per chunk of a row in the
+// split-KV pass; 64-key tiles):
 //  * the 64 records of a tile (64 x 656 B) are gathered with 16-byte loads
-//    into registers one tile ahead, then stored to LDS as a linear array,
-//    so consecutive lanes read consecutive 16 B of a record and write
-//    consecutive 16 B of LDS;
-//  * QK^T: wave w scores keys 16w..16w+15 of the tile for all 16 head rows
-//    with v_mfma_f32_16x16x32_bf16.  E4M3 codes are exact in bf16; each
-//    key's per-128 tile scale multiplies that tile's float32 partial, so the
-//    logits carry no rounding of code*scale (the pages' kernel applies its
-//    power-of-two scales to the operand instead);
+//    into registers one tile ahead (4 threads per record), then stored to
+//    LDS as 64 consecutive records; the slot ids of the tile after that are
+//    loaded a tile earlier still;
+//  * QK^T: wave w scores keys 16w..16w+15 of the tile for all 16 head rows.
+//    The latent part runs on the records' E4M3 codes as they are, with the
+//    block-scaled fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the query is
+//    split once per row into two E4M3 terms with power-of-two block scales
+//    (hi + lo, about 2^-19 relative to its 32-element group's max), and each
+//    key's per-128 tile scale multiplies that tile's float32 partial.  The
+//    rope part is a bf16 MFMA;
 //  * the 16x64 logits go through LDS; every wave computes the online-softmax
 //    weights of the whole tile in the exp2 domain (scale * log2 e, as the
-//    FlyDSL launcher passes it) and keeps identical running max / sum;
+//    FlyDSL launcher passes it) and keeps identical running max / sum; the
+//    running reference only moves when a logit passes it by 2^8;
 //  * PV: wave w owns latent tile w (128 columns) and computes
-//    O^T[d, h] += V^T[d, key] P^T[key, h]; P is multiplied by the key's
-//    scale of tile w before its bf16 rounding, and V^T comes straight from
-//    the record bytes in LDS with the gfx950 transposing LDS read
-//    (ds_read_b64_tr_b8), so each lane ends up owning one head;
-//  * rows longer than the launch needs are split over workgroups, whose
-//    float32 partials and base-2 LSEs are merged by merge_kernel.
+//    O^T[d, h] += V^T[d, key] P^T[key, h] with v_mfma_f32_16x16x32_bf16;
+//    P is multiplied by the key's scale of tile w before its bf16 rounding,
+//    and V^T comes straight from the record bytes in LDS with the gfx950
+//    transposing LDS read (ds_read_b64_tr_b8) and an exact E4M3 -> bf16
+//    conversion, so each lane ends up owning one head;
+//  * when there are too few rows to fill the GPU, rows are cut into chunks
+//    planned on the device (split_plan), each chunk's float32 partial and
+//    base-2 LSE go to a workspace, and merge_kernel combines them.
 #include "device_utils.h"
 #include "mla_internal.h"
 
