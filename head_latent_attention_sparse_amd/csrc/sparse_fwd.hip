@@ -110,10 +110,28 @@ __device__ __forceinline__ int32_t ceil_div_rcp(int32_t len, int32_t c, float rc
   return q + (r > 0 ? 1 : 0);
 }
 
+// Sum and inclusive prefix sum over the 64 lanes of a wave (all lanes
+// active): DPP row shifts within each 16-lane row, then row broadcasts of
+// lanes 15 and 31 into the rows above.  A lane without a source adds 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  v += dpp_i32<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_i32<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_i32<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_i32<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_i32<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i32<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ int32_t wave_sum(int32_t v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
+
 struct SplitPlanLds {
-  unsigned long long n;
-  int32_t rows;
-  int32_t cnt[kPlanCandidates];
+  uint32_t n[4];  // per wave: sum of lengths (exact for a non-decreasing indptr: < 2^29)
+  int32_t rows[4];
+  int32_t cnt[kPlanCandidates][4];
   int32_t wave_tot[4];
   int32_t hit[3];  // row, begin, end of this workgroup's chunk
 };
@@ -126,11 +144,12 @@ __device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t,
   const int32_t tokens = p.tokens;
   const int32_t r0 = 2 * tid;
 
+  // rows r0 and r0 + 1: three offsets, one round trip
   int32_t len[2] = {0, 0}, rb[2] = {0, 0};
   if (r0 < tokens) {
-    const int64_t x0 = (int64_t)indptr[r0], x1 = (int64_t)indptr[r0 + 1];
-    const int64_t x2 = r0 + 1 < tokens ? (int64_t)indptr[r0 + 2] : x1;
-    const int64_t xs[3] = {x0, x1, x2};
+    const IdxT x0 = indptr[r0], x1 = indptr[r0 + 1], x2 = indptr[r0 + 1 < tokens ? r0 + 2 : r0 + 1];
+    __builtin_amdgcn_sched_barrier(0);  // all three loads in flight before any use
+    const int64_t xs[3] = {(int64_t)x0, (int64_t)x1, (int64_t)x2};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int64_t b = xs[i], e = xs[i + 1];
@@ -139,24 +158,22 @@ __device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t,
       rb[i] = (int32_t)b;  // nnz < 2^29
       len[i] = (int32_t)(e - b);
     }
-    if (r0 + 1 >= tokens) len[1] = 0;
   }
-  if (tid == 0) {
-    sh.n = 0;
-    sh.rows = 0;
-#pragma unroll
-    for (int k = 0; k < kPlanCandidates; ++k) sh.cnt[k] = 0;
-  }
-  __syncthreads();
 
   int32_t chunk = p.forced_chunk;
   if (chunk <= 0) {
-    if (len[0] + len[1] > 0) {
-      atomicAdd(&sh.n, (unsigned long long)(len[0] + len[1]));
-      atomicAdd(&sh.rows, (len[0] > 0) + (len[1] > 0));
+    // For a malformed (decreasing) indptr the sums may wrap; every chunk size
+    // below is still in [kMinChunk, 2^29], and the caps keep chunks in range.
+    const int32_t nw = wave_sum(len[0] + len[1]);
+    const int32_t rw = wave_sum((len[0] > 0) + (len[1] > 0));
+    if (lane == 0) {
+      sh.n[wave] = (uint32_t)nw;
+      sh.rows[wave] = rw;
     }
     __syncthreads();
-    const int64_t n = (int64_t)sh.n, rows = sh.rows, bound = p.bound;
+    const int64_t n = (int64_t)(sh.n[0] + sh.n[1] + sh.n[2] + sh.n[3]);
+    const int64_t rows = sh.rows[0] + sh.rows[1] + sh.rows[2] + sh.rows[3];
+    const int64_t bound = p.bound;
     const int64_t lo = max(kMinChunk, ((n + bound - 1) / bound + 63) & ~(int64_t)63);
     const int64_t slack = bound > rows ? bound - rows : 1;
     const int64_t hi = min(max(lo, ((n + slack - 1) / slack + 63) & ~(int64_t)63), (int64_t)1 << 29);
@@ -165,25 +182,20 @@ __device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t,
     for (int k = 0; k < kPlanCandidates; ++k) {
       const int32_t c = (int32_t)min(lo + step * k, hi);
       const float rcp = 1.0f / (float)c;
-      const int32_t cnt = ceil_div_rcp(len[0], c, rcp) + ceil_div_rcp(len[1], c, rcp);
-      if (cnt) atomicAdd(&sh.cnt[k], cnt);
+      const int32_t cw = wave_sum(ceil_div_rcp(len[0], c, rcp) + ceil_div_rcp(len[1], c, rcp));
+      if (lane == 0) sh.cnt[k][wave] = cw;
     }
     __syncthreads();
     chunk = (int32_t)hi;  // always fits
 #pragma unroll
     for (int k = kPlanCandidates - 1; k >= 0; --k)
-      if (sh.cnt[k] <= bound) chunk = (int32_t)min(lo + step * k, hi);
+      if (sh.cnt[k][0] + sh.cnt[k][1] + sh.cnt[k][2] + sh.cnt[k][3] <= bound) chunk = (int32_t)min(lo + step * k, hi);
   }
 
   // first chunk of each row: one block scan of this thread's two counts
   const float rcp = 1.0f / (float)chunk;
   const int32_t c0 = ceil_div_rcp(len[0], chunk, rcp), c1 = ceil_div_rcp(len[1], chunk, rcp);
-  int32_t incl = c0 + c1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t u = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += u;
-  }
+  const int32_t incl = wave_incl_scan(c0 + c1);
   if (lane == 63) sh.wave_tot[wave] = incl;
   __syncthreads();
   int64_t first0 = incl - c0 - c1;
@@ -309,33 +321,36 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
   };
 
-  // ---- start the first tile early: the slots of tiles 0 and 1 (for the
-  // masks) and this thread's record of tile 0 are requested before the
-  // query, and tile 0's gather is issued before the query split is computed,
-  // so these round trips overlap instead of following one another.
+  // ---- start the first tile early.  The query is requested first, then
+  // this thread's slot of tile 0 and the slots of tiles 0 and 1 (for the
+  // masks); tile 0's gather is issued as soon as its slot is in, and the
+  // query split is computed while the gather is in flight.  (The gather is
+  // conditional, so anything loaded after it would wait for it.)  Query loads
+  // are unconditional: a lane past the last head reads the last head's row
+  // and zeroes it.
+  const int nq = n < p.heads ? n : p.heads - 1;
+  const uint32_t qkeep = n < p.heads ? 0xFFFFFFFFu : 0u;
+  const uint16_t *qrow = p.q + t * p.q_st + (int64_t)nq * p.q_sh;
+  // rope part: bf16 MFMA A operand (row = head n); lane (n, g) k-slots j of
+  // step st <-> rope d = 16g + 8st + j; the record's rope bytes are read with
+  // the same mapping.
+  u32x4_t qr[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + kLatent + 16 * g + 8 * st);
+    qr[st] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
+  }
+  // latent part: the 32 values of (head n, latent tile `wave`, k-block g)
+  uint32_t qx[16];
+  {
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * wave + 32 * g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) qx[e] = src[e] & qkeep;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the slot loads
+  const IdxT my_id0 = fetch_entry(0, grec);
   const IdxT slot_t0 = fetch_entry(0, lane);
   const IdxT slot_t1 = fetch_entry(1, lane);
-  const IdxT my_id0 = fetch_entry(0, grec);
-
-  // ---- query, rope part: bf16 MFMA A operand (row = head n); lane (n, g)
-  // k-slots j of step st <-> rope d = 16g + 8st + j; the record's rope bytes
-  // are read with the same mapping.
-  u32x4_t qr[2];
-  {
-    const uint32_t *qrow = reinterpret_cast<const uint32_t *>(p.q + t * p.q_st + (int64_t)n * p.q_sh);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (n < p.heads) {
-        const uint32_t *src = qrow + ((kLatent + 16 * g + 8 * st) >> 1);
-        v.x = src[0];
-        v.y = src[1];
-        v.z = src[2];
-        v.w = src[3];
-      }
-      qr[st] = v;
-    }
-  }
 
   // ---- query, latent part: two E4M3 terms per 32-element group, so that
   // QK^T runs on the records' E4M3 codes directly (scaled fp8 MFMA, no code
@@ -354,18 +369,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   {
     uint8_t *q_lds = s_rec;                     // [(blk * 2 + part) * 16 + h][128] codes
     uint8_t *sc_lds = s_rec + 4 * 2 * 16 * 128;  // [(part * 16 + h) * 4 + kb] words, byte blk
-    float x[32];
-    {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(p.q + t * p.q_st + (int64_t)n * p.q_sh +
-                                                               128 * wave + 32 * g);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t w2 = n < p.heads ? src[e] : 0u;
-        x[2 * e] = as_float(w2 << 16);
-        x[2 * e + 1] = as_float(w2 & 0xFFFF0000u);
-      }
-    }
     issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0, in flight during the split
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x[2 * e] = as_float(qx[e] << 16);
+      x[2 * e + 1] = as_float(qx[e] & 0xFFFF0000u);
+    }
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
