@@ -1,13 +1,15 @@
 """Benchmark of the sparse MLA forward on MI355X (one GPU).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                [--no-cpu-baseline] [--copy-calibration]
+                [--no-cpu-baseline] [--copy-calibration] [--epilogue]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
 4096 rows; for the insert + attend workload it is the insert of the new
-tokens followed by the forward.  Inputs are synthetic, seeded, and resident
-in HBM before timing starts.  Prints ONE JSON line.
+tokens followed by the forward.  With --epilogue a step is instead one
+decode epilogue call (mla_decode_q_concat_insert: 4096 tokens, 16 heads,
+RoPE).  Inputs are synthetic, seeded, and resident in HBM before timing
+starts.  Prints ONE JSON line.
 """
 
 import argparse
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="measure the decode epilogue (query concat + RoPE + insert) instead of the forward")
     return ap.parse_args()
 
 
@@ -72,6 +76,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.epilogue:
+        bench_epilogue(args, dev)
+        return
     log(f"generating workload {args.config}")
     w = workloads.CONFIGS[args.config]()
     t_count, heads = w.num_tokens, w.num_heads
@@ -187,6 +194,92 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def time_steps(step, args, stream):
+    """W untimed steps, then K steps with a HIP event pair each on `stream`;
+    returns (wall ms per step, mean device ms per step)."""
+    import numpy as np
+    import torch
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / args.steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def bench_epilogue(args, dev):
+    """One decode epilogue call per step: mqa_q = [ql_nope | RoPE(q_pe)] and the
+    insert of [kv_c | RoPE(k_pe)], 4096 tokens x 16 heads into 131072 records."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    log("generating the decode epilogue inputs")
+    w = workloads.decode_epilogue()
+    b, h = w.ql_nope.shape[0], w.ql_nope.shape[1]
+    ql, qp, kv, kp = w.ql_nope.to(dev), w.q_pe.to(dev), w.kv_c.to(dev), w.k_pe.to(dev)
+    slots, pos, table = w.slots.to(dev), w.positions.to(dev), w.cos_sin_cache.to(dev)
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=dev)
+    mqa = torch.empty((b, h, 576), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mla.decode_q_concat_insert(ql, qp, kv, kp, pool, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
+
+    ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
+    kept = int(((w.slots >= 0) & (w.slots < w.num_records)).sum())
+    # algorithmic bytes: every input once (the token's cos/sin row included),
+    # mqa_q once, one record per kept token
+    read = b * (h * 576 * 2 + 512 * 2 + 64 * 2 + 8 + 8 + 64 * 4)
+    written = b * h * 576 * 2 + kept * 656
+    achieved = (read + written) / (dev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "MLA decode epilogue (query concat + GPT-J RoPE + fp8_ds_mla insert): tokens/s",
+        "value": b / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode epilogue: B={b} tokens, H={h}, RoPE from a 65536-position fp32 table, "
+                               f"{w.num_records} records, 5% slots skipped", "parallelism": "single GPU"},
+        "device_ms_per_step": dev_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": read + written},
+    }
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import decode_q_concat_insert
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        bits = [bf16_bits(x) for x in (w.ql_nope, w.q_pe, w.kv_c, w.k_pe)]
+        opool = np.zeros((w.num_records, 656), dtype=np.uint8)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            decode_q_concat_insert(*bits, w.slots.numpy(), opool, w.positions.numpy(), w.cos_sin_cache.numpy())
+            el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": b / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole call ({b} tokens), numpy oracle, one thread, {el:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

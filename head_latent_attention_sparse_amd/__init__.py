@@ -11,10 +11,12 @@ from .ops import (  # noqa: F401
     KV_LORA_RANK,
     MAX_HEADS,
     MAX_CHUNK_TILES,
+    MAX_EPILOGUE_HEADS,
     QK_ROPE_HEAD_DIM,
     RECORD_BYTES,
     MlaError,
     cache_insert,
+    decode_q_concat_insert,
     lib,
     split_workgroups,
     sparse_fwd,

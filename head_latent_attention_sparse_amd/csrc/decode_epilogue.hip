@@ -1,0 +1,102 @@
+// MLA decode epilogue for gfx950: the latent decode query
+// mqa_q = [ql_nope | RoPE(q_pe)] and the fp8_ds_mla insert of
+// [kv_c_normed | RoPE(k_pe)], in one launch.
+//
+// What it computes is fused_mla_decode_q_concat_kv_cache_insert with
+// ds_mla=True (vLLM API page
+// vllm.models.kimi_k3.nvidia.ops.fused_mla_key_concat_kv_cache, function
+// docstring and its dispatch by cache format: bf16 mqa_q, 656-byte
+// block-scaled cache).  The optional positions / cos_sin_cache pair selects
+// GPT-J-style RoPE (the module docstring), read from an fp32 table and
+// computed in fp32 (vllm.models.kimi_k3.nvidia.mla page,
+// MultiHeadLatentAttention: a float32 table, is_neox_style=False, passed
+// straight to the fused epilogues): for pair i of the
+// 64 rope values, (x0, x1) = (x[2i], x[2i+1]), c = cos_sin[pos][i],
+// s = cos_sin[pos][32 + i],
+//     y[2i]   = x0 * c - x1 * s,    y[2i+1] = x1 * c + x0 * s,
+// each product and the sum rounded to float32 (no fused multiply-add), then
+// to bf16 round-to-nearest-even.
+//
+// One workgroup per token: wave 0 writes the record (write_record_wave),
+// then all four waves copy the query, 16 bytes per thread per step.
+#include "mla_internal.h"
+#include "record_writer.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunksPerHead = kQkDim / 8;  // 72 x 8 bf16
+
+#pragma clang fp contract(off)
+// GPT-J rotation of one pair, float32 with a rounding after every operation.
+__device__ __forceinline__ void rope_pair(float x0, float x1, float c, float s, float &y0, float &y1) {
+  y0 = x0 * c - x1 * s;
+  y1 = x1 * c + x0 * s;
+}
+#pragma clang fp contract(on)
+
+__device__ __forceinline__ uint32_t rope_word(uint32_t w, float c, float s) {
+  float y0, y1;
+  rope_pair(as_float(w << 16), as_float(w & 0xFFFF0000u), c, s, y0, y1);
+  return pack_bf16x2(y0, y1);
+}
+
+__global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogueArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const float *cs = nullptr;  // this token's cos/sin row, or none
+  if (a.positions) {
+    int64_t pos = a.positions[b];
+    pos = pos < 0 ? 0 : (pos >= a.max_position ? a.max_position - 1 : pos);
+    cs = a.cos_sin + pos * kRope;
+  }
+
+  // ---- the record (wave 0)
+  if (tid < 64) {
+    const int64_t slot = a.slots[b];
+    if (slot >= 0 && slot < a.num_records) {
+      const int lane = tid;
+      const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
+      uint32_t w = lane < 32 ? pe[lane] : 0u;
+      if (cs && lane < 32) w = rope_word(w, cs[lane], cs[32 + lane]);
+      write_record_wave(lane, a.kv_c + b * a.kv_c_stride, w, a.records + slot * kRecordBytes);
+    }
+  }
+
+  // ---- the query: chunk j of head h holds columns 8j .. 8j+7 of the 576
+  const int chunks = a.num_heads * kChunksPerHead;
+  for (int c = tid; c < chunks; c += kThreads) {
+    const int h = c / kChunksPerHead;
+    const int j = c - h * kChunksPerHead;
+    uint32_t w[4];
+    if (j < kLatent / 8) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.ql_nope + b * a.ql_stride_token +
+                                                               (int64_t)h * a.ql_stride_head + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = src[i];
+    } else {
+      const int jr = j - kLatent / 8;  // rope pairs 4jr .. 4jr+3
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.q_pe + b * a.qpe_stride_token +
+                                                               (int64_t)h * a.qpe_stride_head + 8 * jr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = src[i];
+      if (cs) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = rope_word(w[i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
+      }
+    }
+    uint32_t *dst = reinterpret_cast<uint32_t *>(a.mqa_q + b * a.mq_stride_token + (int64_t)h * a.mq_stride_head + 8 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = w[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_epilogue(const DecodeEpilogueArgs &a, hipStream_t stream) {
+  decode_epilogue_kernel<<<dim3((unsigned)a.num_tokens), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -47,6 +47,29 @@ struct InsertArgs {
 
 hipError_t launch_cache_insert(const InsertArgs &a, hipStream_t stream);
 
+struct DecodeEpilogueArgs {
+  const uint16_t *ql_nope;
+  int64_t ql_stride_token, ql_stride_head;  // elements
+  const uint16_t *q_pe;
+  int64_t qpe_stride_token, qpe_stride_head;
+  const uint16_t *kv_c;
+  int64_t kv_c_stride;
+  const uint16_t *k_pe;
+  int64_t k_pe_stride;
+  const int64_t *slots;
+  int64_t num_tokens;
+  int32_t num_heads;
+  const int64_t *positions;  // nullptr: no RoPE
+  const float *cos_sin;      // [max_position, 64]: cos of pair i at i, sin at 32 + i
+  int64_t max_position;
+  uint16_t *mqa_q;
+  int64_t mq_stride_token, mq_stride_head;
+  uint8_t *records;
+  int64_t num_records;
+};
+
+hipError_t launch_decode_epilogue(const DecodeEpilogueArgs &a, hipStream_t stream);
+
 // Workspace of a chunked (split-KV) call, in 256-byte aligned parts:
 // partials, partial LSEs, row prefix.
 struct SplitLayout {

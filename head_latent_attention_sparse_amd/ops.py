@@ -7,7 +7,8 @@ and the current stream.  There is no fallback: if libmla.so is missing or
 fails to load, every call raises.
 
 Names and keyword arguments follow flydsl_sparse_mla_fp8ds_fwd on the
-flydsl_sparse_mla page and the ds_mla insert on the
+flydsl_sparse_mla page and the ds_mla insert and decode epilogue
+(fused_mla_decode_q_concat_kv_cache_insert) on the
 fused_mla_key_concat_kv_cache page.
 """
 
@@ -24,6 +25,7 @@ KV_LORA_RANK = 512
 QK_ROPE_HEAD_DIM = 64
 MAX_HEADS = 16
 MAX_CHUNK_TILES = 65535
+MAX_EPILOGUE_HEADS = 1024
 
 FLAG_HAS_INVALID = 1 << 0
 FLAG_RETURN_LSE = 1 << 1
@@ -43,6 +45,8 @@ SIGNATURES = {
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "mla_decode_q_concat_insert": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P,
+                                          _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
     "mla_abi_version": (_I32, []),
@@ -222,3 +226,77 @@ def cache_insert(kv_c, k_pe, slot_mapping, kv_cache):
                                 slot_mapping.data_ptr(), n, kv_ptr, n_rec, pitch, _stream(kv_c.device))
     _check(st)
     return kv_cache
+
+
+def _bf16_rows(x, name, shape_tail, device):
+    """Check a CUDA bf16 tensor whose last dim is contiguous; returns it."""
+    if not (torch.is_tensor(x) and x.dtype == torch.bfloat16 and x.device == device):
+        raise ValueError(f"{name} must be a bf16 tensor on {device}")
+    if tuple(x.shape[1:]) != tuple(shape_tail) or x.stride(-1) != 1:
+        raise ValueError(f"{name} must be [B, {', '.join(map(str, shape_tail))}] with a contiguous last dim")
+    return x
+
+
+def decode_q_concat_insert(ql_nope, q_pe, kv_c_normed, k_pe, kv_cache, slot_mapping, *, positions=None,
+                           cos_sin_cache=None, mqa_q=None):
+    """MLA decode epilogue in one launch -> mqa_q [B, H, 576] bf16.
+
+    mqa_q = [ql_nope | q_pe], and [kv_c_normed | k_pe] is inserted into the
+    fp8_ds_mla cache at slot_mapping (negative = skip), with GPT-J RoPE on
+    q_pe and k_pe when ``positions`` [B] int64 and the fp32
+    ``cos_sin_cache`` [max_position, 64] are given.  ql_nope [B, H, 512],
+    q_pe [B, H, 64], kv_c_normed [B, 512], k_pe [B, 64] or [B, 1, 64], all
+    bf16 with a contiguous last dim.
+    """
+    if not (torch.is_tensor(ql_nope) and ql_nope.is_cuda and ql_nope.ndim == 3):
+        raise ValueError("ql_nope must be a CUDA bf16 tensor [B, H, 512]")
+    dev = ql_nope.device
+    b, heads = ql_nope.shape[0], ql_nope.shape[1]
+    if not 1 <= heads <= MAX_EPILOGUE_HEADS:
+        raise ValueError(f"{heads} heads: 1 .. {MAX_EPILOGUE_HEADS} are served")
+    _bf16_rows(ql_nope, "ql_nope", (heads, KV_LORA_RANK), dev)
+    _bf16_rows(q_pe, "q_pe", (heads, QK_ROPE_HEAD_DIM), dev)
+    _bf16_rows(kv_c_normed, "kv_c_normed", (KV_LORA_RANK,), dev)
+    if not (torch.is_tensor(k_pe) and k_pe.numel() == b * QK_ROPE_HEAD_DIM):
+        raise ValueError("k_pe must hold 64 values per token")
+    k_pe2 = _bf16_rows(k_pe.reshape(b, QK_ROPE_HEAD_DIM), "k_pe", (QK_ROPE_HEAD_DIM,), dev)
+    for name, x in (("q_pe", q_pe), ("kv_c_normed", kv_c_normed), ("k_pe", k_pe2)):
+        if x.shape[0] != b:
+            raise ValueError(f"{name} must have {b} tokens")
+    if not (torch.is_tensor(slot_mapping) and slot_mapping.dtype == torch.int64 and slot_mapping.ndim == 1
+            and slot_mapping.numel() == b and slot_mapping.is_contiguous() and slot_mapping.device == dev):
+        raise ValueError("slot_mapping must be a contiguous int64 [B] tensor on ql_nope's device")
+    if (positions is None) != (cos_sin_cache is None):
+        raise ValueError("positions and cos_sin_cache come together")
+    max_position = 0
+    if positions is not None:
+        if not (positions.dtype == torch.int64 and positions.ndim == 1 and positions.numel() == b
+                and positions.is_contiguous() and positions.device == dev):
+            raise ValueError("positions must be a contiguous int64 [B] tensor on ql_nope's device")
+        if not (cos_sin_cache.dtype == torch.float32 and cos_sin_cache.ndim == 2
+                and cos_sin_cache.shape[1] == QK_ROPE_HEAD_DIM and cos_sin_cache.is_contiguous()
+                and cos_sin_cache.device == dev):
+            raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, 64] tensor")
+        max_position = cos_sin_cache.shape[0]
+    if mqa_q is None:
+        mqa_q = torch.empty((b, heads, KV_LORA_RANK + QK_ROPE_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _bf16_rows(mqa_q, "mqa_q", (heads, KV_LORA_RANK + QK_ROPE_HEAD_DIM), dev)
+        if mqa_q.shape[0] != b:
+            raise ValueError(f"mqa_q must have {b} tokens")
+    if not (torch.is_tensor(kv_cache) and kv_cache.device == dev):
+        raise ValueError("kv cache must be on ql_nope's device")
+    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    L = lib()
+    with torch.cuda.device(dev):
+        st = L.mla_decode_q_concat_insert(
+            ql_nope.data_ptr(), ql_nope.stride(0), ql_nope.stride(1),
+            q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1),
+            kv_c_normed.data_ptr(), kv_c_normed.stride(0), k_pe2.data_ptr(), k_pe2.stride(0),
+            slot_mapping.data_ptr(), b, heads,
+            positions.data_ptr() if positions is not None else None,
+            cos_sin_cache.data_ptr() if cos_sin_cache is not None else None, max_position,
+            mqa_q.data_ptr(), mqa_q.stride(0), mqa_q.stride(1),
+            kv_ptr, n_rec, pitch, _stream(dev))
+    _check(st)
+    return mqa_q

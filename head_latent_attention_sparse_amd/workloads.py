@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five sparse-MLA workloads.
+"""Seeded synthetic inputs for the five sparse-MLA workloads and the decode epilogue.
 
 This module only draws random numbers and lays them out (CSR lists, block
 tables, slot mappings).  It holds none of the method's arithmetic, so the
@@ -188,6 +188,45 @@ def insert_attend(pool: int = 65536, new_tokens: int = 4096, p_skip: float = 0.0
     return Workload("insert_attend", pool, q, indptr, indices, SOFTMAX_SCALE,
                     has_invalid=False, return_lse=True, setup_inserts=[fill],
                     step_inserts=[InsertBatch(kv_c, k_pe, slots)])
+
+
+@dataclass
+class DecodeEpilogueBatch:
+    """Inputs of one decode epilogue call (query concat + RoPE + insert)."""
+    ql_nope: torch.Tensor         # bf16 [B, H, 512]
+    q_pe: torch.Tensor            # bf16 [B, H, 64]
+    kv_c: torch.Tensor            # bf16 [B, 512]
+    k_pe: torch.Tensor            # bf16 [B, 64]
+    slots: torch.Tensor           # int64 [B], -1 = skip
+    positions: torch.Tensor       # int64 [B]
+    cos_sin_cache: torch.Tensor   # float32 [max_position, 64]
+    num_records: int
+
+
+def rope_table(max_position: int, dim: int = ROPE, base: float = 10000.0) -> torch.Tensor:
+    """A rotary table as a model builds one: row p holds cos(p * f_i) for the
+    dim/2 frequencies f_i = base^(-2i/dim), then sin(p * f_i); computed in
+    float64 and stored as float32.  (Input data: the epilogue only reads it.)"""
+    inv_freq = base ** (-torch.arange(0, dim, 2, dtype=torch.float64) / dim)
+    ang = torch.arange(max_position, dtype=torch.float64)[:, None] * inv_freq[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32)
+
+
+def decode_epilogue(batch: int = 4096, heads: int = 16, pool: int = 131072, max_position: int = 65536,
+                    p_skip: float = 0.05, seed_offset: int = 6) -> DecodeEpilogueBatch:
+    """A decode epilogue call: B tokens with H heads of absorbed query
+    (ql_nope N(0,1), q_pe N(0,1)), their latent N(0,1) and rope N(0,1), at
+    distinct random slots of a pool (each -1 with probability p_skip), at
+    random positions below max_position, with a standard rotary table."""
+    g = torch.Generator().manual_seed(SEED_BASE + seed_offset)
+    ql_nope = _bf16(g, (batch, heads, LATENT))
+    q_pe = _bf16(g, (batch, heads, ROPE))
+    kv_c = _bf16(g, (batch, LATENT))
+    k_pe = _bf16(g, (batch, ROPE))
+    slots = torch.randperm(pool, generator=g)[:batch].to(torch.int64)
+    slots[torch.rand(batch, generator=g) < p_skip] = -1
+    positions = torch.randint(0, max_position, (batch,), generator=g, dtype=torch.int64)
+    return DecodeEpilogueBatch(ql_nope, q_pe, kv_c, k_pe, slots, positions, rope_table(max_position), pool)
 
 
 CONFIGS = {

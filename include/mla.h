@@ -177,6 +177,54 @@ mla_status_t mla_cache_insert(const void *kv_c, int64_t kv_c_stride_token,
                               void *kv_records, int64_t num_records, int64_t record_stride,
                               void *stream);
 
+/*
+ * mla_decode_q_concat_insert - the MLA decode epilogue in one launch: the
+ * latent decode query mqa_q = [ql_nope | RoPE(q_pe)] and the insert of
+ * [kv_c_normed | RoPE(k_pe)] into the fp8_ds_mla cache.
+ *
+ * Defined by fused_mla_decode_q_concat_kv_cache_insert with ds_mla=True
+ * (fused_mla_key_concat_kv_cache page, function docstring: bf16 mqa_q and
+ * the 656-byte block-scaled cache, one launch, right before the latent
+ * attention).  With positions and cos_sin_cache, GPT-J-style RoPE (module
+ * docstring) is applied to q_pe and k_pe in float32 from the fp32 table
+ * (vllm.models.kimi_k3.nvidia.mla page, MultiHeadLatentAttention): pair i = (x[2i], x[2i+1]) of the 64 rope
+ * values, c = cos_sin_cache[pos][i], s = cos_sin_cache[pos][32 + i],
+ *     y[2i] = x[2i]*c - x[2i+1]*s,   y[2i+1] = x[2i+1]*c + x[2i]*s,
+ * each product and sum rounded to float32 (no fused multiply-add), the
+ * result rounded to bf16 (nearest even).  Without them q_pe and k_pe are
+ * copied bit for bit.  The record is written as by mla_cache_insert, with
+ * the rotated k_pe as its rope part; a token with a negative slot or a slot
+ * >= num_records writes mqa_q only.
+ *
+ *  ql_nope      bf16 [num_tokens, num_heads, 512], element (b,h,d) at
+ *               ql_nope + b*ql_stride_token + h*ql_stride_head + d.
+ *  q_pe         bf16 [num_tokens, num_heads, 64], likewise.
+ *  kv_c         bf16 [num_tokens, 512], row stride kv_c_stride_token.
+ *  k_pe         bf16 [num_tokens, 64], row stride k_pe_stride_token.
+ *  slot_mapping int64 [num_tokens], 8-byte aligned.
+ *  num_tokens   >= 0; 0 returns MLA_OK and queues nothing.
+ *  num_heads    1 .. MLA_MAX_EPILOGUE_HEADS.
+ *  positions    int64 [num_tokens] or NULL; a position outside
+ *               [0, max_position) is clamped into it (keeps reads in the table).
+ *  cos_sin_cache float32 [max_position, 64] (row b: 32 cosines, then 32
+ *               sines), contiguous, 4-byte aligned; NULL exactly when
+ *               positions is NULL.
+ *  mqa_q        bf16 output [num_tokens, num_heads, 576], element (b,h,d) at
+ *               mqa_q + b*mqa_stride_token + h*mqa_stride_head + d.
+ *  kv_records   as for mla_sparse_fwd (written in place).
+ * Strides are in elements, even and >= 0; bf16 bases 4-byte aligned.
+ * Two tokens with the same slot race, as in mla_cache_insert.
+ */
+#define MLA_MAX_EPILOGUE_HEADS 1024
+mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_token, int64_t ql_stride_head,
+                                        const void *q_pe, int64_t q_pe_stride_token, int64_t q_pe_stride_head,
+                                        const void *kv_c, int64_t kv_c_stride_token, const void *k_pe,
+                                        int64_t k_pe_stride_token, const int64_t *slot_mapping, int64_t num_tokens,
+                                        int32_t num_heads, const int64_t *positions, const float *cos_sin_cache,
+                                        int64_t max_position, void *mqa_q, int64_t mqa_stride_token,
+                                        int64_t mqa_stride_head, void *kv_records, int64_t num_records,
+                                        int64_t record_stride, void *stream);
+
 /* Message for the last failed call on this thread ("" if none).  Host memory
  * owned by the library, valid until the thread's next failing call. */
 const char *mla_last_error(void);
@@ -185,7 +233,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -18,12 +18,16 @@ vLLM API pages:
   (``fused_mla_key_concat_ds_mla_insert`` docstring): the self-scaling
   record writer with per-128-tile dynamic fp8 scales;
 * ``vllm.models.kimi_k3.nvidia.mla`` (``_compute_prefill_context`` and
-  ``merge_attn_states`` call): combining attention partials by their LSEs.
+  ``merge_attn_states`` call): combining attention partials by their LSEs;
+* ``fused_mla_decode_q_concat_kv_cache_insert`` (same fused_mla_key_concat
+  page) and ``MultiHeadLatentAttention`` on the ``vllm.models.kimi_k3.nvidia.mla``
+  page: the decode epilogue's query concat and GPT-J RoPE in float32.
 
 Modules:
   e4m3       OCP float8 E4M3 ("fn") decode table and saturating RNE encoder.
   records    656-byte record encode (the insert writer) and decode.
   attention  Sparse attention forward over records, and the LSE merge.
+  epilogue   Decode epilogue: mqa_q concat, GPT-J RoPE, record insert.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -36,3 +40,4 @@ from .records import (  # noqa: F401
     insert_records,
 )
 from .attention import merge_partials, sparse_fwd  # noqa: F401
+from .epilogue import decode_q_concat_insert, f32_to_bf16_bits, rope_gptj_bits  # noqa: F401

@@ -158,3 +158,43 @@ def test_workspace_size_of_forced_chunks_needs_no_device():
     assert lib.mla_sparse_fwd_workspace_size(8, 16, 1000, 4 << 16, 0) == want
     assert lib.mla_sparse_fwd_workspace_size(0, 16, 0, 4 << 16, 0) == 0
     assert lib.mla_sparse_fwd_workspace_size(8, 17, 1000, 4 << 16, 0) == ctypes.c_size_t(-1).value
+
+
+def epilogue(**kw):
+    args = dict(ql=A, qlt=16 * 512, qlh=512, qp=A, qpt=16 * 64, qph=64, kv=A, kvt=512, kp=A, kpt=64, slots=A, T=8,
+                H=16, pos=None, cs=None, maxpos=0, mq=A, mqt=16 * 576, mqh=576, rec=A, n=100, pitch=656, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_decode_q_concat_insert(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=0), UNSUPPORTED),
+    (dict(H=1025), UNSUPPORTED),
+    (dict(T=-1), INVALID),
+    (dict(qlh=511), UNSUPPORTED),
+    (dict(qpt=-64), INVALID),
+    (dict(mqh=577), UNSUPPORTED),
+    (dict(ql=A + 2), UNSUPPORTED),
+    (dict(mq=A + 2), UNSUPPORTED),
+    (dict(pitch=672), UNSUPPORTED),
+    (dict(rec=A + 8), UNSUPPORTED),
+    (dict(n=-1), INVALID),
+    (dict(slots=A + 4), INVALID),
+    (dict(pos=A), INVALID),                        # positions without a table
+    (dict(cs=A, maxpos=16), INVALID),              # a table without positions
+    (dict(pos=A, cs=A, maxpos=0), INVALID),
+    (dict(pos=A + 4, cs=A, maxpos=16), INVALID),
+    (dict(ql=None), INVALID),
+    (dict(mq=None), INVALID),
+])
+def test_epilogue_rejections(kw, status):
+    st, msg = epilogue(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_epilogue_zero_tokens_is_a_no_op():
+    st, _ = epilogue(T=0, ql=None, qp=None, kv=None, kp=None, slots=None, mq=None)
+    assert st == OK
