@@ -1,14 +1,15 @@
 """Benchmark of the sparse MLA forward on MI355X (one GPU).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                [--no-cpu-baseline] [--copy-calibration] [--epilogue]
+                [--no-cpu-baseline] [--copy-calibration] [--epilogue | --gather]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
 4096 rows; for the insert + attend workload it is the insert of the new
 tokens followed by the forward.  With --epilogue a step is instead one
 decode epilogue call (mla_decode_q_concat_insert: 4096 tokens, 16 heads,
-RoPE).  Inputs are synthetic, seeded, and resident in HBM before timing
+RoPE), and with --gather one context-chunk gather + upconvert
+(mla_gather_upconvert: 64 requests of 1024..8192 tokens).  Inputs are synthetic, seeded, and resident in HBM before timing
 starts.  Prints ONE JSON line.
 """
 
@@ -48,6 +49,8 @@ def parse():
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--epilogue", action="store_true",
                     help="measure the decode epilogue (query concat + RoPE + insert) instead of the forward")
+    ap.add_argument("--gather", action="store_true",
+                    help="measure the context gather + upconvert to bf16 instead of the forward")
     return ap.parse_args()
 
 
@@ -78,6 +81,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.epilogue:
         bench_epilogue(args, dev)
+        return
+    if args.gather:
+        bench_gather(args, dev)
         return
     log(f"generating workload {args.config}")
     w = workloads.CONFIGS[args.config]()
@@ -280,6 +286,74 @@ def bench_epilogue(args, dev):
             el = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": b / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the whole call ({b} tokens), numpy oracle, one thread, {el:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_gather(args, dev):
+    """One mla_gather_upconvert per step: a context chunk of 64 requests
+    (contexts of 1024..8192 tokens, blocks of 64) into a bf16 [toks, 576]
+    workspace."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    log("generating the context gather inputs")
+    w = workloads.context_gather()
+    pool = torch.zeros((w.num_records // w.block_size, w.block_size, 656), dtype=torch.uint8, device=dev)
+    for b in w.setup_inserts:
+        mla.cache_insert(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev), pool)
+    table, cu, starts = w.block_table.to(dev), w.cu_seq_lens.to(dev), w.seq_starts.to(dev)
+    n = w.num_tokens
+    dst = torch.empty((n, 576), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mla.gather_upconvert(pool, table, cu, n, seq_starts=starts, dst=dst)
+
+    ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
+    moved = n * (656 + 576 * 2)  # each row: one record read, one bf16 row written
+    achieved = moved / (dev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "context gather + upconvert (fp8_ds_mla records -> bf16 workspace): tokens/s",
+        "value": n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"context gather: 64 requests, contexts U[1024,8192], blocks of 64, {n} tokens",
+                   "parallelism": "single GPU"},
+        "device_ms_per_step": dev_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
+    }
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import encode_records, gather_upconvert
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        with threadpool_limits(limits=1):
+            # the pool by the oracle's own writer (untimed setup)
+            opool = np.zeros((w.num_records, 656), dtype=np.uint8)
+            for b in w.setup_inserts:
+                kv, pe, sl = bf16_bits(b.kv_c), bf16_bits(b.k_pe), b.slots.numpy()
+                for i in range(0, sl.size, 8192):
+                    opool[sl[i:i + 8192]] = encode_records(kv[i:i + 8192], pe[i:i + 8192])
+            t0 = time.perf_counter()
+            gather_upconvert(opool, w.block_size, w.block_table.numpy(), w.cu_seq_lens.numpy(),
+                             w.seq_starts.numpy(), n)
+            el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole chunk ({n} tokens), numpy oracle, one thread, {el:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

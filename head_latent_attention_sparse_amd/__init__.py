@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     MlaError,
     cache_insert,
     decode_q_concat_insert,
+    gather_upconvert,
     lib,
     split_workgroups,
     sparse_fwd,

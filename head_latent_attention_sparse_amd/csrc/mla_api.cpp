@@ -361,4 +361,46 @@ mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_t
   return MLA_OK;
 }
 
+mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, int64_t record_stride,
+                                  int64_t block_size, const int32_t *block_table, int64_t block_table_stride,
+                                  int64_t block_table_width, const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                                  int32_t batch_size, int64_t num_tokens, void *dst, int64_t dst_stride_token,
+                                  void *stream) {
+  const char *fn = "mla_gather_upconvert";
+  if (num_tokens < 0 || num_records < 0 || batch_size < 0 || block_table_width < 0 || block_table_stride < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative size or stride", fn);
+  if (block_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: block_size %lld < 1", fn, (long long)block_size);
+  if (record_stride != MLA_RECORD_BYTES)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: record pitch %lld, only %d (unpadded) is served", fn, (long long)record_stride,
+                MLA_RECORD_BYTES);
+  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "%s: kv_records base not 16-byte aligned", fn);
+  if (!aligned(dst, 16) || dst_stride_token % 8 != 0 || dst_stride_token < MLA_QK_DIM)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: dst must be 16-byte aligned with a row stride >= 576 and a multiple of 8", fn);
+  if (!aligned(block_table, 4) || !aligned(cu_seq_lens, 4) || !aligned(seq_starts, 4))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: misaligned int32 array", fn);
+  if (num_tokens == 0) return MLA_OK;
+  if (num_tokens > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  if (!dst) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL dst", fn);
+  if (batch_size > 0 && !cu_seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL cu_seq_lens", fn);
+  if (batch_size > 0 && block_table_width > 0 && !block_table)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL block_table", fn);
+  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL kv_records", fn);
+  mla::GatherArgs a;
+  a.records = static_cast<const uint8_t *>(kv_records);
+  a.num_records = num_records;
+  a.block_size = block_size;
+  a.block_table = block_table;
+  a.bt_stride = block_table_stride;
+  a.bt_width = block_table ? block_table_width : 0;
+  a.cu = cu_seq_lens;
+  a.starts = seq_starts;
+  a.batch = cu_seq_lens ? batch_size : 0;
+  a.num_tokens = num_tokens;
+  a.dst = static_cast<uint16_t *>(dst);
+  a.dst_stride = dst_stride_token;
+  hipError_t e = mla::launch_gather_upconvert(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // extern "C"

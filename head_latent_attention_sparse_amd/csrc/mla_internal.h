@@ -70,6 +70,23 @@ struct DecodeEpilogueArgs {
 
 hipError_t launch_decode_epilogue(const DecodeEpilogueArgs &a, hipStream_t stream);
 
+struct GatherArgs {
+  const uint8_t *records;
+  int64_t num_records;
+  int64_t block_size;
+  const int32_t *block_table;
+  int64_t bt_stride;  // elements between requests' rows
+  int64_t bt_width;   // blocks per row
+  const int32_t *cu;  // [batch + 1] workspace row of each request's first token
+  const int32_t *starts;  // [batch] first context position of each request, or nullptr (0)
+  int32_t batch;
+  int64_t num_tokens;
+  uint16_t *dst;
+  int64_t dst_stride;  // elements
+};
+
+hipError_t launch_gather_upconvert(const GatherArgs &a, hipStream_t stream);
+
 // Workspace of a chunked (split-KV) call, in 256-byte aligned parts:
 // partials, partial LSEs, row prefix.
 struct SplitLayout {

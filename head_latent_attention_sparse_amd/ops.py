@@ -45,6 +45,7 @@ SIGNATURES = {
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "mla_gather_upconvert": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _I32, _I64, _P, _I64, _P]),
     "mla_decode_q_concat_insert": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P,
                                           _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
@@ -300,3 +301,48 @@ def decode_q_concat_insert(ql_nope, q_pe, kv_c_normed, k_pe, kv_cache, slot_mapp
             kv_ptr, n_rec, pitch, _stream(dev))
     _check(st)
     return mqa_q
+
+
+def gather_upconvert(kv_cache, block_table, cu_seq_lens, num_tokens, *, seq_starts=None, block_size=None,
+                     dst=None):
+    """Gather a context chunk through the block table -> bf16 [num_tokens, 576].
+
+    kv_cache: the paged pool [num_blocks, block_size, 656] (or a flat record
+    view with ``block_size`` given); block_table int32 [B, W];
+    cu_seq_lens int32 [B + 1] (the chunk's workspace rows); seq_starts int32
+    [B] or None.  Row cu[r] + j holds context position seq_starts[r] + j of
+    request r, as [dequantized latent | rope] in bf16; rows with no valid
+    source are zero.
+    """
+    if not (torch.is_tensor(kv_cache) and kv_cache.is_cuda):
+        raise ValueError("kv cache must be a CUDA tensor")
+    dev = kv_cache.device
+    if block_size is None:
+        if kv_cache.ndim != 3:
+            raise ValueError("pass block_size for a kv cache that is not [num_blocks, block_size, 656]")
+        block_size = kv_cache.shape[1]
+    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    if not (torch.is_tensor(block_table) and block_table.dtype == torch.int32 and block_table.ndim == 2
+            and block_table.device == dev and block_table.stride(1) == 1):
+        raise ValueError("block_table must be an int32 [B, W] tensor with contiguous rows on the cache's device")
+    batch = block_table.shape[0]
+    for name, x, n in (("cu_seq_lens", cu_seq_lens, batch + 1), ("seq_starts", seq_starts, batch)):
+        if x is None and name == "seq_starts":
+            continue
+        if not (torch.is_tensor(x) and x.dtype == torch.int32 and x.ndim == 1 and x.numel() == n
+                and x.is_contiguous() and x.device == dev):
+            raise ValueError(f"{name} must be a contiguous int32 [{n}] tensor on the cache's device")
+    if dst is None:
+        dst = torch.empty((num_tokens, KV_LORA_RANK + QK_ROPE_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    elif not (dst.dtype == torch.bfloat16 and dst.ndim == 2 and dst.shape[0] == num_tokens
+              and dst.shape[1] == KV_LORA_RANK + QK_ROPE_HEAD_DIM and dst.stride(1) == 1 and dst.device == dev):
+        raise ValueError("dst must be bf16 [num_tokens, 576] with contiguous rows on the cache's device")
+    L = lib()
+    with torch.cuda.device(dev):
+        st = L.mla_gather_upconvert(
+            kv_ptr, n_rec, pitch, int(block_size),
+            block_table.data_ptr() if block_table.numel() else None, block_table.stride(0), block_table.shape[1],
+            cu_seq_lens.data_ptr(), seq_starts.data_ptr() if seq_starts is not None else None, batch,
+            num_tokens, dst.data_ptr() if num_tokens else None, dst.stride(0), _stream(dev))
+    _check(st)
+    return dst

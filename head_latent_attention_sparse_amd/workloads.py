@@ -229,6 +229,47 @@ def decode_epilogue(batch: int = 4096, heads: int = 16, pool: int = 131072, max_
     return DecodeEpilogueBatch(ql_nope, q_pe, kv_c, k_pe, slots, positions, rope_table(max_position), pool)
 
 
+@dataclass
+class ContextGatherBatch:
+    """Inputs of one context-chunk gather: a paged pool and its requests."""
+    setup_inserts: List[InsertBatch]  # build the pool from zero bytes
+    num_records: int
+    block_size: int
+    block_table: torch.Tensor   # int32 [B, W]; unused entries -1
+    cu_seq_lens: torch.Tensor   # int32 [B + 1]
+    seq_starts: torch.Tensor    # int32 [B]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.cu_seq_lens[-1])
+
+
+def context_gather(batch: int = 64, len_lo: int = 1024, len_hi: int = 8192, block_size: int = 64,
+                   start_frac: float = 0.0, seed_offset: int = 7) -> ContextGatherBatch:
+    """A context chunk over a paged pool: context lengths uniform on
+    [len_lo, len_hi], a random permutation of the pool's blocks dealt to the
+    requests in order (as in the paged decode workload); the chunk of request
+    b starts at a uniform position below start_frac * length and runs to the
+    end of its context."""
+    g = torch.Generator().manual_seed(SEED_BASE + seed_offset)
+    lengths = torch.randint(len_lo, len_hi + 1, (batch,), generator=g)
+    blocks_per = [(int(n) + block_size - 1) // block_size for n in lengths]
+    num_blocks = sum(blocks_per)
+    fill = _pool_fill(g, num_blocks * block_size)
+    perm = torch.randperm(num_blocks, generator=g).to(torch.int32)
+    width = max(blocks_per) if blocks_per else 0
+    table = torch.full((batch, width), -1, dtype=torch.int32)
+    start = 0
+    for b, nb in enumerate(blocks_per):
+        table[b, :nb] = perm[start:start + nb]
+        start += nb
+    hi = (lengths.to(torch.float64) * start_frac).to(torch.int64) + 1
+    starts = (torch.rand(batch, generator=g, dtype=torch.float64) * hi).to(torch.int64).clamp(max=lengths - 1)
+    counts = lengths - starts
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(counts, 0)]).to(torch.int32)
+    return ContextGatherBatch([fill], num_blocks * block_size, block_size, table, cu, starts.to(torch.int32))
+
+
 CONFIGS = {
     1: tiny,
     2: paged_decode,

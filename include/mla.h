@@ -225,6 +225,41 @@ mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_t
                                         int64_t mqa_stride_head, void *kv_records, int64_t num_records,
                                         int64_t record_stride, void *stream);
 
+/*
+ * mla_gather_upconvert - gather a context chunk's records through the block
+ * table into a bf16 [num_tokens, 576] workspace (dequantized latent | rope).
+ *
+ * Defined by cp_gather_and_upconvert_fp8_kv_cache as the kimi_k3 nvidia mla
+ * page calls it in _gather_context_latent (src_cache, dst = workspace[:toks],
+ * block_table, workspace_starts = the chunk's cu_seq_lens, batch_size,
+ * seq_starts): for request r and j < cu_seq_lens[r+1] - cu_seq_lens[r],
+ * context position p = seq_starts[r] + j (seq_starts NULL: 0) is read from
+ * record block_table[r][p / block_size] * block_size + p % block_size and
+ * written to row cu_seq_lens[r] + j as
+ *     dst[row, d]       = bf16(f32(E4M3(code[d])) * scale[d / 128]), d < 512
+ *     dst[row, 512 + i] = rope[i] (bit copy), i < 64
+ * (float32 product, then bf16 round to nearest even: the model dtype of the
+ * workspace).  Rows of [0, num_tokens) with no valid source - outside every
+ * request, a position past block_table_width, a block id < 0 or a slot
+ * >= num_records - are written as zeros.
+ *
+ *  kv_records   the record pool (num_records records at record_stride = 656
+ *               bytes, 16-byte aligned base), as for mla_sparse_fwd.
+ *  block_size   records per block (>= 1).
+ *  block_table  int32 [batch_size, >= block_table_width], row r at
+ *               block_table + r*block_table_stride.
+ *  cu_seq_lens  int32 [batch_size + 1], non-decreasing workspace rows.
+ *  seq_starts   int32 [batch_size] first context position per request, or NULL.
+ *  dst          bf16 [num_tokens, 576] output, 16-byte aligned, row stride
+ *               dst_stride_token elements (a multiple of 8, >= 576).
+ *  num_tokens   rows to write, 0 .. 2^31 - 1 (0 queues nothing).
+ */
+mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, int64_t record_stride,
+                                  int64_t block_size, const int32_t *block_table, int64_t block_table_stride,
+                                  int64_t block_table_width, const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                                  int32_t batch_size, int64_t num_tokens, void *dst, int64_t dst_stride_token,
+                                  void *stream);
+
 /* Message for the last failed call on this thread ("" if none).  Host memory
  * owned by the library, valid until the thread's next failing call. */
 const char *mla_last_error(void);
@@ -233,7 +268,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -21,13 +21,17 @@ vLLM API pages:
   ``merge_attn_states`` call): combining attention partials by their LSEs;
 * ``fused_mla_decode_q_concat_kv_cache_insert`` (same fused_mla_key_concat
   page) and ``MultiHeadLatentAttention`` on the ``vllm.models.kimi_k3.nvidia.mla``
-  page: the decode epilogue's query concat and GPT-J RoPE in float32.
+  page: the decode epilogue's query concat and GPT-J RoPE in float32;
+* ``cp_gather_and_upconvert_fp8_kv_cache`` as ``_gather_context_latent``
+  calls it (``vllm.models.kimi_k3.nvidia.mla`` page): a context chunk's
+  records, through the block table, into a bf16 workspace.
 
 Modules:
   e4m3       OCP float8 E4M3 ("fn") decode table and saturating RNE encoder.
   records    656-byte record encode (the insert writer) and decode.
   attention  Sparse attention forward over records, and the LSE merge.
   epilogue   Decode epilogue: mqa_q concat, GPT-J RoPE, record insert.
+  gather     Context gather through the block table, upconverted to bf16.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -41,3 +45,4 @@ from .records import (  # noqa: F401
 )
 from .attention import merge_partials, sparse_fwd  # noqa: F401
 from .epilogue import decode_q_concat_insert, f32_to_bf16_bits, rope_gptj_bits  # noqa: F401
+from .gather import gather_upconvert, upconvert_records  # noqa: F401

@@ -198,3 +198,38 @@ def test_epilogue_rejections(kw, status):
 def test_epilogue_zero_tokens_is_a_no_op():
     st, _ = epilogue(T=0, ql=None, qp=None, kv=None, kp=None, slots=None, mq=None)
     assert st == OK
+
+
+def gather(**kw):
+    args = dict(rec=A, n=1024, pitch=656, bs=64, bt=A, bts=16, btw=16, cu=A, starts=None, B=8, T=100, dst=A,
+                dsts=576, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_gather_upconvert(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(bs=0), INVALID),
+    (dict(pitch=660), UNSUPPORTED),
+    (dict(rec=A + 8), UNSUPPORTED),
+    (dict(dst=A + 8), UNSUPPORTED),
+    (dict(dsts=580), UNSUPPORTED),
+    (dict(dsts=512), UNSUPPORTED),
+    (dict(bt=A + 2), INVALID),
+    (dict(cu=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(dst=None), INVALID),
+])
+def test_gather_rejections(kw, status):
+    st, msg = gather(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_gather_zero_tokens_is_a_no_op():
+    st, _ = gather(T=0, dst=None, cu=None, bt=None)
+    assert st == OK
