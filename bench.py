@@ -1,7 +1,7 @@
 """Benchmark of the sparse MLA forward on MI355X (one GPU).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                [--no-cpu-baseline] [--copy-calibration] [--epilogue | --gather]
+                [--no-cpu-baseline] [--copy-calibration] [--epilogue | --gather | --vproj]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
@@ -9,7 +9,9 @@ prefill workload (the default) that is one mla_sparse_fwd call over all
 tokens followed by the forward.  With --epilogue a step is instead one
 decode epilogue call (mla_decode_q_concat_insert: 4096 tokens, 16 heads,
 RoPE), and with --gather one context-chunk gather + upconvert
-(mla_gather_upconvert: 64 requests of 1024..8192 tokens).  Inputs are synthetic, seeded, and resident in HBM before timing
+(mla_gather_upconvert: 64 requests of 1024..8192 tokens), and with --vproj
+one W_UV up-projection with the sigmoid gate (mla_v_up_proj: 4096 rows x 16
+heads).  Inputs are synthetic, seeded, and resident in HBM before timing
 starts.  Prints ONE JSON line.
 """
 
@@ -51,6 +53,8 @@ def parse():
                     help="measure the decode epilogue (query concat + RoPE + insert) instead of the forward")
     ap.add_argument("--gather", action="store_true",
                     help="measure the context gather + upconvert to bf16 instead of the forward")
+    ap.add_argument("--vproj", action="store_true",
+                    help="measure the W_UV up-projection with the sigmoid gate instead of the forward")
     return ap.parse_args()
 
 
@@ -84,6 +88,9 @@ def main():
         return
     if args.gather:
         bench_gather(args, dev)
+        return
+    if args.vproj:
+        bench_vproj(args, dev)
         return
     log(f"generating workload {args.config}")
     w = workloads.CONFIGS[args.config]()
@@ -354,6 +361,67 @@ def bench_gather(args, dev):
             el = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the whole chunk ({n} tokens), numpy oracle, one thread, {el:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_vproj(args, dev):
+    """One mla_v_up_proj per step: [4096, 16, 512] latent times W_UV [16, 512, 128],
+    gated by sigmoid of a [4096, 2048] gate."""
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    log("generating the up-projection inputs")
+    w = workloads.v_up_proj_inputs()
+    lat, wuv, gate = w.latent.to(dev), w.w_uv.to(dev), w.gate.to(dev)
+    t, h = lat.shape[0], lat.shape[1]
+    out = torch.empty((t, h, 128), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mla.v_up_proj(lat, wuv, gate=gate, out=out)
+
+    ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
+    moved = lat.numel() * 2 + wuv.numel() * 2 + gate.numel() * 2 + out.numel() * 2
+    flops = 2.0 * t * h * 512 * 128
+    achieved = moved / (dev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "W_UV up-projection + sigmoid gate: rows/s",
+        "value": t / (ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"v up-projection: T={t} rows, H={h}, latent 512 -> v 128, gated",
+                   "parallelism": "single GPU"},
+        "device_ms_per_step": dev_ms,
+        "mfma_tflops": flops / (dev_ms * 1e-3) / 1e12,
+        "mfma_frac": flops / (dev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
+    }
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import v_up_proj
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        lb, wb, gb = bf16_bits(w.latent), bf16_bits(w.w_uv), bf16_bits(w.gate)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            v_up_proj(lb, wb, gb)
+            el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": t / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole call ({t} rows x {h} heads), numpy float64 oracle, "
+                                            f"one thread, {el:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -21,4 +21,5 @@ from .ops import (  # noqa: F401
     lib,
     split_workgroups,
     sparse_fwd,
+    v_up_proj,
 )

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["sparse_fwd.hip", "cache_insert.hip", "decode_epilogue.hip", "gather_upconvert.hip", "mla_api.cpp"]
+SOURCES = ["sparse_fwd.hip", "cache_insert.hip", "decode_epilogue.hip", "gather_upconvert.hip", "v_up_proj.hip", "mla_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

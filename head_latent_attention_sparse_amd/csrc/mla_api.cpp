@@ -403,4 +403,41 @@ mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, i
   return MLA_OK;
 }
 
+mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
+                           const void *w_uv, const void *gate, int64_t gate_stride_token, int64_t num_tokens,
+                           int32_t num_heads, void *out, int64_t out_stride_token, int64_t out_stride_head,
+                           void *stream) {
+  const char *fn = "mla_v_up_proj";
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_tokens %lld < 0", fn, (long long)num_tokens);
+  if (num_heads < 1 || num_heads > MLA_MAX_EPILOGUE_HEADS)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: num_heads %d outside 1..%d", fn, num_heads, MLA_MAX_EPILOGUE_HEADS);
+  if (latent_stride_token < 0 || latent_stride_head < 0 || gate_stride_token < 0 || out_stride_token < 0 ||
+      out_stride_head < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative stride", fn);
+  if (!aligned(latent, 16) || latent_stride_token % 8 || latent_stride_head % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: latent must be 16-byte aligned with strides that are multiples of 8", fn);
+  if (!aligned(out, 4) || (out_stride_token | out_stride_head) & 1 || !aligned(w_uv, 2) ||
+      (gate && (!aligned(gate, 4) || (gate_stride_token & 1))))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: out / gate must be 4-byte aligned with even strides", fn);
+  if (num_tokens == 0) return MLA_OK;
+  if (!latent || !w_uv || !out) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL latent, w_uv or out", fn);
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return fail(MLA_ERR_HIP, "%s: hipGetDevice failed", fn);
+  mla::VUpProjArgs a;
+  a.latent = static_cast<const uint16_t *>(latent);
+  a.lat_st = latent_stride_token;
+  a.lat_sh = latent_stride_head;
+  a.w = static_cast<const uint16_t *>(w_uv);
+  a.gate = static_cast<const uint16_t *>(gate);
+  a.gate_st = gate_stride_token;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.out = static_cast<uint16_t *>(out);
+  a.out_st = out_stride_token;
+  a.out_sh = out_stride_head;
+  hipError_t e = mla::launch_v_up_proj(a, device_cus(device), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // extern "C"

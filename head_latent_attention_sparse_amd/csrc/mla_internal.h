@@ -87,6 +87,20 @@ struct GatherArgs {
 
 hipError_t launch_gather_upconvert(const GatherArgs &a, hipStream_t stream);
 
+struct VUpProjArgs {
+  const uint16_t *latent;  // bf16, element (t, h, l) at t*lat_st + h*lat_sh + l
+  int64_t lat_st, lat_sh;
+  const uint16_t *w;       // bf16 [H, 512, 128] contiguous
+  const uint16_t *gate;    // bf16, element (t, h*128 + v) at t*gate_st + h*128 + v, or nullptr
+  int64_t gate_st;
+  int64_t num_tokens;
+  int32_t num_heads;
+  uint16_t *out;           // bf16, element (t, h, v) at t*out_st + h*out_sh + v
+  int64_t out_st, out_sh;
+};
+
+hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t stream);
+
 // Workspace of a chunked (split-KV) call, in 256-byte aligned parts:
 // partials, partial LSEs, row prefix.
 struct SplitLayout {

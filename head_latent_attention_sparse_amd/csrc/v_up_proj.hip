@@ -1,0 +1,226 @@
+// W_UV up-projection of the latent attention output, with the optional
+// sigmoid gate, for gfx950.
+//
+// What it computes is _v_up_proj on the vllm.models.kimi_k3.nvidia.mla page
+// (per head h: [T, 512] latent rows times W_UV[h], the (N, L, V) = [H, 512,
+// 128] weight that process_weights_after_loading splits out of kv_b_proj),
+// followed by the gate of the layer's forward (attn_out times the sigmoid of
+// the g_proj output, [T, H * 128]):
+//     out[t, h, v] = bf16( (sum_l latent[t, h, l] * W_UV[h, l, v]) * sigmoid(gate[t, 128h + v]) )
+// with float32 accumulation on the matrix cores, the gate applied in
+// float32, and one round to nearest even.
+//
+// Memory-bound (about 86 FLOP per byte at H = 16), so the design keeps the
+// latent read exactly once and keeps HBM busy: a workgroup takes one head,
+// holds that head's whole W_UV (128 KB) in registers as MFMA B fragments
+// (wave w owns output columns 32w .. 32w+31; the weight is brought in with
+// coalesced loads and transposed through LDS), and streams 32-row latent
+// tiles and their gate rows with a two-tile register pipeline (loads are
+// unconditional, so each wait covers exactly the tile it needs).  A tile's
+// 32 x 128 float32 result is staged in LDS, so the gate is applied and the
+// output written in coalesced 16-byte pieces.
+#include "device_utils.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kV = 128;                          // v_head_dim
+constexpr int kTileRows = 32;
+constexpr int kKSteps = kLatent / 32;            // 16 MFMA k-steps of 32
+constexpr int kAPitch = kLatent + 8;             // bf16 per LDS latent row (1040 B: conflict-free 16-B reads)
+constexpr int kOPitch = kV + 4;                  // floats per LDS output row
+constexpr int kWRows = 128;                      // W_UV rows per transposition pass
+constexpr int kWPitch = kV + 4;                  // bf16 per LDS weight row (264 B)
+constexpr int kABytes = kTileRows * kAPitch * 2;
+constexpr int kOBytes = kTileRows * kOPitch * 4;
+constexpr int kWBytes = kWRows * kWPitch * 2;
+constexpr int kSmem = (kABytes + kOBytes) > kWBytes ? (kABytes + kOBytes) : kWBytes;
+constexpr int kLatChunks = kTileRows * kLatent / 8 / kThreads;  // 8 x 16 B of latent per thread and tile
+constexpr int kOutChunks = kTileRows * kV / 8 / kThreads;       // 2 x 8 outputs per thread and tile
+static_assert(kWRows * kV / 8 / kThreads == 8, "weight pass: 8 chunks per thread");
+
+struct TileRegs {
+  u32x4_t lat[kLatChunks];
+  u32x4_t gate[kOutChunks];
+};
+
+template <bool kGate>
+__global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  uint16_t *s_a = reinterpret_cast<uint16_t *>(smem);
+  float *s_o = reinterpret_cast<float *>(smem + kABytes);
+  uint16_t *s_w = reinterpret_cast<uint16_t *>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y;
+  const int64_t tiles = (a.num_tokens + kTileRows - 1) / kTileRows;
+
+  // ---- tile loads.  Latent chunk q = tid + 256k of the tile's 32 x 64
+  // 16-byte chunks: row q / 64, chunk q % 64 (a wave reads a whole row).
+  // Output / gate chunk q = tid + 256k of 32 x 16: row q / 16, chunk q % 16.
+  // A tile index past the end reloads the last tile, and rows past the end
+  // repeat the last row, so every load is unconditional and in bounds.
+  auto load_tile = [&](int64_t tile, TileRegs &r) {
+    tile = tile < tiles ? tile : tiles - 1;
+#pragma unroll
+    for (int k = 0; k < kLatChunks; ++k) {
+      const int q = tid + kThreads * k;
+      int64_t row = tile * kTileRows + (q >> 6);
+      row = row < a.num_tokens ? row : a.num_tokens - 1;
+      r.lat[k] = *reinterpret_cast<const u32x4_t *>(a.latent + row * a.lat_st + (int64_t)h * a.lat_sh + 8 * (q & 63));
+    }
+    if (kGate) {
+#pragma unroll
+      for (int k = 0; k < kOutChunks; ++k) {
+        const int q = tid + kThreads * k;
+        int64_t row = tile * kTileRows + (q >> 4);
+        row = row < a.num_tokens ? row : a.num_tokens - 1;
+        const uint32_t *gp = reinterpret_cast<const uint32_t *>(a.gate + row * a.gate_st + (int64_t)h * kV + 8 * (q & 15));
+        r.gate[k] = u32x4_t{gp[0], gp[1], gp[2], gp[3]};
+      }
+    }
+  };
+
+  // the first two tiles load while the weights are set up
+  const int64_t step = gridDim.x;
+  TileRegs r0, r1;
+  int64_t tile = blockIdx.x;
+  load_tile(tile, r0);
+  load_tile(tile + step, r1);
+
+  // ---- W_UV[h] as B fragments: bw[s][j] holds, for lane (c, g), rows
+  // 32s + 8g .. +7 of column 32 * wave + 16j + c.  Four passes of 128 rows:
+  // coalesced 16-byte loads into LDS (pitch 264 B: the 4 row groups of a
+  // read land 16 banks apart), then 2-byte reads down the columns.
+  bf16x8_t bw[kKSteps][2];
+  {
+    const uint16_t *w = a.w + (int64_t)h * kLatent * kV;
+    u32x4_t wr[kLatent / kWRows][8];  // every pass's loads in flight at once
+#pragma unroll
+    for (int pass = 0; pass < kLatent / kWRows; ++pass)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int q = tid + kThreads * k;  // row q / 16, chunk q % 16 of the pass
+        wr[pass][k] = *reinterpret_cast<const u32x4_t *>(w + (int64_t)(kWRows * pass + (q >> 4)) * kV + 8 * (q & 15));
+      }
+#pragma unroll
+    for (int pass = 0; pass < kLatent / kWRows; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's reads are done
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int q = tid + kThreads * k;
+        uint32_t *d = reinterpret_cast<uint32_t *>(s_w + (q >> 4) * kWPitch + 8 * (q & 15));
+        *reinterpret_cast<u32x2_t *>(d) = u32x2_t{wr[pass][k].x, wr[pass][k].y};
+        *reinterpret_cast<u32x2_t *>(d + 2) = u32x2_t{wr[pass][k].z, wr[pass][k].w};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int sl = 0; sl < kWRows / 32; ++sl) {
+        const int s = pass * (kWRows / 32) + sl;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint16_t *col = s_w + (32 * sl + 8 * g) * kWPitch + 32 * wave + 16 * j + c;
+          uint32_t v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (uint32_t)col[(2 * e) * kWPitch] | ((uint32_t)col[(2 * e + 1) * kWPitch] << 16);
+          bw[s][j] = as_bf16x8(u32x4_t{v[0], v[1], v[2], v[3]});
+        }
+      }
+    }
+    __syncthreads();  // the weight staging area becomes the tile buffers
+  }
+
+  auto compute_tile = [&](int64_t tile, const TileRegs &r) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int k = 0; k < kLatChunks; ++k) {
+      const int q = tid + kThreads * k;
+      *reinterpret_cast<u32x4_t *>(s_a + (q >> 6) * kAPitch + 8 * (q & 63)) = r.lat[k];
+    }
+    __syncthreads();
+    floatx4_t acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u32x4_t *>(s_a + (16 * m + c) * kAPitch + 32 * s + 8 * g));
+        acc[m][0] = mfma_16x16x32_bf16(af, bw[s][0], acc[m][0]);
+        acc[m][1] = mfma_16x16x32_bf16(af, bw[s][1], acc[m][1]);
+      }
+    }
+    // D of m-tile m, n-tile j: lane (c, g) holds rows 16m + 4g + r, column 32 * wave + 16j + c
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[(16 * m + 4 * g + i) * kOPitch + 32 * wave + 16 * j + c] = acc[m][j][i];
+    __syncthreads();
+    // All results first, then unconditional stores: a store counts in the
+    // same counter as the loads, and a conditional one would make every later
+    // wait assume it was not issued (so waits would cover the prefetched
+    // tiles too).  A row past the end was computed from the last row's
+    // latent and gate (the loads clamp), so it holds exactly the last row's
+    // bits and is stored there, rewriting the same value.
+    uint32_t res[kOutChunks][4];
+#pragma unroll
+    for (int k = 0; k < kOutChunks; ++k) {
+      const int q = tid + kThreads * k;
+      const int rr = q >> 4, ch = q & 15;
+      const floatx4_t y0 = *reinterpret_cast<const floatx4_t *>(s_o + rr * kOPitch + 8 * ch);
+      const floatx4_t y1 = *reinterpret_cast<const floatx4_t *>(s_o + rr * kOPitch + 8 * ch + 4);
+      float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      if (kGate) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t gw = r.gate[k][i];
+          y[2 * i] *= __builtin_amdgcn_rcpf(1.0f + __expf(-as_float(gw << 16)));
+          y[2 * i + 1] *= __builtin_amdgcn_rcpf(1.0f + __expf(-as_float(gw & 0xFFFF0000u)));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) res[k][i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+    }
+#pragma unroll
+    for (int k = 0; k < kOutChunks; ++k) {
+      const int q = tid + kThreads * k;
+      int64_t row = tile * kTileRows + (q >> 4);
+      row = row < a.num_tokens ? row : a.num_tokens - 1;
+      uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + row * a.out_st + (int64_t)h * a.out_sh + 8 * (q & 15));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = res[k][i];
+    }
+  };
+
+  // ---- two tiles in flight: while tile i is computed, tiles i+1 and i+2
+  // are loading (into the register set tile i used, once it is in LDS).
+  for (; tile < tiles; tile += 2 * step) {
+    compute_tile(tile, r0);
+    load_tile(tile + 2 * step, r0);
+    if (tile + step >= tiles) break;
+    compute_tile(tile + step, r1);
+    load_tile(tile + 3 * step, r1);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t stream) {
+  const int64_t tiles = (a.num_tokens + kTileRows - 1) / kTileRows;
+  // one workgroup per CU in all (each holds a head's weights in registers)
+  int64_t per_head = (num_cus > 0 ? num_cus : 256) / a.num_heads;
+  per_head = per_head < 1 ? 1 : (per_head > tiles ? tiles : per_head);
+  const dim3 grid((unsigned)per_head, (unsigned)a.num_heads);
+  if (a.gate)
+    v_up_proj_kernel<true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else
+    v_up_proj_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -45,6 +45,7 @@ SIGNATURES = {
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
+    "mla_v_up_proj": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _I64, _I64, _P]),
     "mla_gather_upconvert": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _I32, _I64, _P, _I64, _P]),
     "mla_decode_q_concat_insert": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P,
                                           _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
@@ -346,3 +347,40 @@ def gather_upconvert(kv_cache, block_table, cu_seq_lens, num_tokens, *, seq_star
             num_tokens, dst.data_ptr() if num_tokens else None, dst.stride(0), _stream(dev))
     _check(st)
     return dst
+
+
+V_HEAD_DIM = 128
+
+
+def v_up_proj(latent, w_uv, *, gate=None, out=None):
+    """out[t, h, :] = latent[t, h, :512] @ w_uv[h] (times sigmoid(gate)) -> bf16 [T, H, 128].
+
+    latent: bf16 [T, H, >= 512] (e.g. sparse_fwd's out) with a contiguous last
+    dim, 16-byte aligned rows; w_uv: bf16 [H, 512, 128] contiguous; gate:
+    bf16 [T, H * 128] with a contiguous last dim, or None.
+    """
+    if not (torch.is_tensor(latent) and latent.is_cuda and latent.dtype == torch.bfloat16 and latent.ndim == 3
+            and latent.shape[2] >= KV_LORA_RANK and latent.stride(2) == 1):
+        raise ValueError("latent must be a CUDA bf16 [T, H, >= 512] tensor with a contiguous last dim")
+    dev = latent.device
+    t_count, heads = latent.shape[0], latent.shape[1]
+    if not 1 <= heads <= MAX_EPILOGUE_HEADS:
+        raise ValueError(f"{heads} heads: 1 .. {MAX_EPILOGUE_HEADS} are served")
+    if not (torch.is_tensor(w_uv) and w_uv.dtype == torch.bfloat16 and w_uv.device == dev
+            and tuple(w_uv.shape) == (heads, KV_LORA_RANK, V_HEAD_DIM) and w_uv.is_contiguous()):
+        raise ValueError(f"w_uv must be a contiguous bf16 [{heads}, 512, 128] tensor on latent's device")
+    if gate is not None and not (torch.is_tensor(gate) and gate.dtype == torch.bfloat16 and gate.device == dev
+                                 and tuple(gate.shape) == (t_count, heads * V_HEAD_DIM) and gate.stride(1) == 1):
+        raise ValueError(f"gate must be bf16 [{t_count}, {heads * V_HEAD_DIM}] with a contiguous last dim")
+    if out is None:
+        out = torch.empty((t_count, heads, V_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    elif not (out.dtype == torch.bfloat16 and out.device == dev and out.ndim == 3 and out.shape[0] == t_count
+              and out.shape[1] == heads and out.shape[2] >= V_HEAD_DIM and out.stride(2) == 1):
+        raise ValueError("out must be bf16 [T, H, >= 128] with a contiguous last dim")
+    L = lib()
+    with torch.cuda.device(dev):
+        st = L.mla_v_up_proj(latent.data_ptr(), latent.stride(0), latent.stride(1), w_uv.data_ptr(),
+                             gate.data_ptr() if gate is not None else None, gate.stride(0) if gate is not None else 0,
+                             t_count, heads, out.data_ptr(), out.stride(0), out.stride(1), _stream(dev))
+    _check(st)
+    return out

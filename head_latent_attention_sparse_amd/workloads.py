@@ -270,6 +270,23 @@ def context_gather(batch: int = 64, len_lo: int = 1024, len_hi: int = 8192, bloc
     return ContextGatherBatch([fill], num_blocks * block_size, block_size, table, cu, starts.to(torch.int32))
 
 
+@dataclass
+class VUpProjBatch:
+    latent: torch.Tensor  # bf16 [T, H, 512]
+    w_uv: torch.Tensor    # bf16 [H, 512, 128]
+    gate: torch.Tensor    # bf16 [T, H * 128]
+
+
+def v_up_proj_inputs(tokens: int = 4096, heads: int = 16, seed_offset: int = 8) -> VUpProjBatch:
+    """Latent attention output N(0,1), a random-init W_UV N(0, 512^-1/2)
+    (so the projection has unit scale), and a gate N(0,1); all bf16."""
+    g = torch.Generator().manual_seed(SEED_BASE + seed_offset)
+    latent = _bf16(g, (tokens, heads, LATENT))
+    w_uv = _bf16(g, (heads, LATENT, 128), std=LATENT**-0.5)
+    gate = _bf16(g, (tokens, heads * 128))
+    return VUpProjBatch(latent, w_uv, gate)
+
+
 CONFIGS = {
     1: tiny,
     2: paged_decode,

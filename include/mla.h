@@ -260,6 +260,34 @@ mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, i
                                   int32_t batch_size, int64_t num_tokens, void *dst, int64_t dst_stride_token,
                                   void *stream);
 
+/*
+ * mla_v_up_proj - project the latent attention output back to v with
+ * W_UV, optionally times the sigmoid gate:
+ *     out[t,h,v] = bf16( (sum_l latent[t,h,l] * w_uv[h,l,v]) * sigmoid(gate[t, 128h + v]) )
+ * (float32 accumulation; without a gate the sigmoid factor is 1; one round
+ * to nearest even).
+ *
+ * Defined by _v_up_proj on the vllm.models.kimi_k3.nvidia.mla page (the
+ * per-head bmm of the [T, H, 512] latent output with W_UV, the (N, L, V)
+ * weight process_weights_after_loading splits from kv_b_proj) and the
+ * layer's gate (forward: attn_out = _gate_sigmoid_mul(attn_out, gate), the
+ * gate being g_proj's [T, H * 128] output); v_head_dim is 128.
+ *
+ *  latent       bf16, element (t,h,l) at latent + t*latent_stride_token +
+ *               h*latent_stride_head + l, l < 512; 16-byte aligned base,
+ *               strides multiples of 8 (e.g. mla_sparse_fwd's out).
+ *  w_uv         bf16 [num_heads, 512, 128] contiguous.
+ *  gate         bf16, element (t, 128h + v) at gate + t*gate_stride_token +
+ *               128h + v, or NULL (no gate).  4-byte aligned, even stride.
+ *  out          bf16, element (t,h,v) at out + t*out_stride_token +
+ *               h*out_stride_head + v, v < 128; 4-byte aligned, even strides.
+ *  num_tokens   >= 0 (0 queues nothing); num_heads 1 .. MLA_MAX_EPILOGUE_HEADS.
+ */
+mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
+                           const void *w_uv, const void *gate, int64_t gate_stride_token, int64_t num_tokens,
+                           int32_t num_heads, void *out, int64_t out_stride_token, int64_t out_stride_head,
+                           void *stream);
+
 /* Message for the last failed call on this thread ("" if none).  Host memory
  * owned by the library, valid until the thread's next failing call. */
 const char *mla_last_error(void);
@@ -268,7 +296,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

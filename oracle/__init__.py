@@ -24,7 +24,10 @@ vLLM API pages:
   page: the decode epilogue's query concat and GPT-J RoPE in float32;
 * ``cp_gather_and_upconvert_fp8_kv_cache`` as ``_gather_context_latent``
   calls it (``vllm.models.kimi_k3.nvidia.mla`` page): a context chunk's
-  records, through the block table, into a bf16 workspace.
+  records, through the block table, into a bf16 workspace;
+* ``_v_up_proj``, ``process_weights_after_loading`` and the gate of
+  ``forward`` (``vllm.models.kimi_k3.nvidia.mla`` page): the W_UV
+  up-projection and the sigmoid gate.
 
 Modules:
   e4m3       OCP float8 E4M3 ("fn") decode table and saturating RNE encoder.
@@ -32,6 +35,7 @@ Modules:
   attention  Sparse attention forward over records, and the LSE merge.
   epilogue   Decode epilogue: mqa_q concat, GPT-J RoPE, record insert.
   gather     Context gather through the block table, upconverted to bf16.
+  value      W_UV up-projection of the latent output, with the sigmoid gate.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -46,3 +50,4 @@ from .records import (  # noqa: F401
 from .attention import merge_partials, sparse_fwd  # noqa: F401
 from .epilogue import decode_q_concat_insert, f32_to_bf16_bits, rope_gptj_bits  # noqa: F401
 from .gather import gather_upconvert, upconvert_records  # noqa: F401
+from .value import v_up_proj  # noqa: F401

@@ -233,3 +233,37 @@ def test_gather_rejections(kw, status):
 def test_gather_zero_tokens_is_a_no_op():
     st, _ = gather(T=0, dst=None, cu=None, bt=None)
     assert st == OK
+
+
+def vproj(**kw):
+    args = dict(lat=A, lst=16 * 512, lsh=512, w=A, gate=None, gst=0, T=64, H=16, out=A, ost=16 * 128, osh=128,
+                stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_v_up_proj(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), INVALID),
+    (dict(H=0), UNSUPPORTED),
+    (dict(H=1025), UNSUPPORTED),
+    (dict(lst=-8), INVALID),
+    (dict(lsh=516), UNSUPPORTED),
+    (dict(lat=A + 8), UNSUPPORTED),
+    (dict(out=A + 2), UNSUPPORTED),
+    (dict(osh=129), UNSUPPORTED),
+    (dict(gate=A + 2, gst=2048), UNSUPPORTED),
+    (dict(gate=A, gst=2049), UNSUPPORTED),
+    (dict(lat=None), INVALID),
+    (dict(w=None), INVALID),
+])
+def test_v_up_proj_rejections(kw, status):
+    st, msg = vproj(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_v_up_proj_zero_tokens_is_a_no_op():
+    st, _ = vproj(T=0, lat=None, w=None, out=None)
+    assert st == OK
