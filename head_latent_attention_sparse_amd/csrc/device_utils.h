@@ -22,6 +22,7 @@ constexpr int kQkDim = 576;
 constexpr int kScaleOffset = 512;
 constexpr int kRopeOffset = 528;
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.44269504088896341f;
 
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }

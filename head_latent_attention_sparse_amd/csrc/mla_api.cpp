@@ -113,9 +113,175 @@ int64_t plan_split(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags, int
   return target;
 }
 
+// The second segment and the sink of mla_sparse_fwd_ex (all absent for mla_sparse_fwd).
+struct FwdExtra {
+  const float *sink = nullptr;
+  const void *records = nullptr;
+  int64_t num_records = 0, record_stride = MLA_RECORD_BYTES;
+  const void *indptr = nullptr, *indices = nullptr;
+  int64_t num_indices = 0;
+};
+
+mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                             int64_t q_stride_head, const void *kv_records, int64_t num_records, int64_t record_stride,
+                             const void *kv_indptr, const void *kv_indices, int64_t num_indices, float softmax_scale,
+                             uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream, const FwdExtra &x) {
+  if (flags & ~kKnownFlags) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: unknown flag bits 0x%x", flags & ~kKnownFlags);
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens > INT32_MAX - 1) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_tokens %lld too large", (long long)num_tokens);
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_heads %d outside 1..%d", num_heads, MLA_MAX_HEADS);
+  if (q_stride_token < 0 || q_stride_head < 0 || out_stride_token < 0 || out_stride_head < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: negative stride");
+  if ((q_stride_token | q_stride_head) & 1)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q strides must be even (got %lld, %lld)", (long long)q_stride_token,
+                (long long)q_stride_head);
+  if ((out_stride_token | out_stride_head) & 1)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out strides must be even (got %lld, %lld)",
+                (long long)out_stride_token, (long long)out_stride_head);
+  if (record_stride != MLA_RECORD_BYTES)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
+                MLA_RECORD_BYTES);
+  if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_records %lld < 0", (long long)num_records);
+  if (num_records > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_records %lld >= 2^31", (long long)num_records);
+  if (num_indices < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_indices %lld < 0", (long long)num_indices);
+  if (num_indices >= MLA_MAX_INDICES)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_indices %lld >= 2^29", (long long)num_indices);
+  const bool i64 = (flags & MLA_FLAG_INDEX_I64) != 0;
+  const bool want_lse = (flags & MLA_FLAG_RETURN_LSE) != 0;
+  const uintptr_t idx_align = i64 ? 8 : 4;
+  const bool has_extra = x.indptr != nullptr;
+  if (has_extra) {
+    if (x.record_stride != MLA_RECORD_BYTES)
+      return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: extra record pitch %lld, only %d is served",
+                  (long long)x.record_stride, MLA_RECORD_BYTES);
+    if (x.num_records < 0 || x.num_indices < 0)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: negative extra size");
+    if (x.num_records > INT32_MAX - 2)
+      return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: extra_num_records %lld >= 2^31 - 2", (long long)x.num_records);
+    if (num_indices + x.num_indices >= MLA_MAX_INDICES)
+      return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_indices + extra_num_indices >= 2^29");
+    if (!aligned(x.records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: extra records not 16-byte aligned");
+    if (!aligned(x.indptr, idx_align) || !aligned(x.indices, idx_align))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: extra index arrays not aligned to their element size");
+    if (x.num_indices > 0 && !x.indices) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL extra_indices");
+    if (x.num_records > 0 && !x.records) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL extra_records");
+  }
+  if (x.sink && !aligned(x.sink, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: attn_sink not 4-byte aligned");
+  const int64_t total_indices = num_indices + (has_extra ? x.num_indices : 0);
+  if (!aligned(q, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q base not 4-byte aligned");
+  if (!aligned(out, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out base not 4-byte aligned");
+  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: kv_records base not 16-byte aligned");
+  if (!aligned(kv_indptr, idx_align) || !aligned(kv_indices, idx_align))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: index arrays not aligned to their element size");
+  if (want_lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: lse not 4-byte aligned");
+  if ((flags & MLA_FLAG_CHUNK_MASK) && num_tokens > mla::kMaxSplitRows)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: forced split-KV serves at most %lld rows",
+                (long long)mla::kMaxSplitRows);
+  if (num_tokens == 0) return MLA_OK;
+  if (!q || !out || !kv_indptr) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL q, out or kv_indptr");
+  if (want_lse && !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: MLA_FLAG_RETURN_LSE with lse == NULL");
+  if (num_indices > 0 && !kv_indices) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_indices");
+  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_records");
+
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: hipGetDevice failed");
+  const bool forced = (flags & MLA_FLAG_CHUNK_MASK) != 0;
+  const int cus = forced ? 0 : device_cus(device);
+  if (!forced && cus <= 0) return fail(MLA_ERR_HIP, "mla_sparse_fwd: cannot query device %d", device);
+  int32_t forced_chunk = 0;
+  const int64_t bound = plan_split(num_tokens, total_indices, cus, flags, &forced_chunk);
+
+  if (bound > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: %lld chunks exceed the grid", (long long)bound);
+
+  mla::FwdArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.q_stride_token = q_stride_token;
+  a.q_stride_head = q_stride_head;
+  a.records = static_cast<const uint8_t *>(kv_records);
+  a.num_records = num_records;
+  a.indptr = kv_indptr;
+  a.indices = num_indices > 0 ? kv_indices : kv_indptr;  // element 0 may be read, never used
+  a.num_indices = num_indices;
+  a.index_i64 = i64;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.num_tokens = (int32_t)num_tokens;
+  a.num_heads = num_heads;
+  a.out = static_cast<uint16_t *>(out);
+  a.out_stride_token = out_stride_token;
+  a.out_stride_head = out_stride_head;
+  a.lse = want_lse ? lse : nullptr;
+  a.chunk_forced = forced_chunk;
+  a.chunk_bound = bound;
+  a.ws_out = nullptr;
+  a.ws_lse = nullptr;
+  a.ws_prefix = nullptr;
+  a.sink = x.sink;
+  if (has_extra) {
+    a.extra_records = static_cast<const uint8_t *>(x.records);
+    a.extra_num_records = x.num_records;
+    a.extra_indptr = x.indptr;
+    a.extra_indices = x.indices;
+    a.extra_num_indices = x.num_indices;
+  }
+  if (bound > 0) {
+    const mla::SplitLayout l = mla::split_layout(num_tokens, num_heads, bound);
+    void *ws = workspace;
+    if (ws) {
+      if (workspace_bytes < l.bytes)
+        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.bytes);
+      if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace not 256-byte aligned");
+    } else {
+      mla_status_t st = workspace_get(device, l.bytes, &ws);
+      if (st != MLA_OK) return st;
+    }
+    char *base = static_cast<char *>(ws);
+    a.ws_out = reinterpret_cast<float *>(base + l.out_off);
+    a.ws_lse = reinterpret_cast<float *>(base + l.lse_off);
+    a.ws_prefix = reinterpret_cast<int32_t *>(base + l.prefix_off);
+  }
+  hipError_t e = mla::launch_sparse_fwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                            int64_t q_stride_head, const void *kv_records, int64_t num_records, int64_t record_stride,
+                            const void *kv_indptr, const void *kv_indices, int64_t num_indices, float softmax_scale,
+                            uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head, float *lse,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return sparse_fwd_impl(q, num_tokens, num_heads, q_stride_token, q_stride_head, kv_records, num_records,
+                         record_stride, kv_indptr, kv_indices, num_indices, softmax_scale, flags, out,
+                         out_stride_token, out_stride_head, lse, workspace, workspace_bytes, stream, FwdExtra());
+}
+
+mla_status_t mla_sparse_fwd_ex(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                               int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                               int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                               int64_t num_indices, const float *attn_sink, const void *extra_records,
+                               int64_t extra_num_records, int64_t extra_record_stride, const void *extra_indptr,
+                               const void *extra_indices, int64_t extra_num_indices, float softmax_scale,
+                               uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head,
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  FwdExtra x;
+  x.sink = attn_sink;
+  x.records = extra_records;
+  x.num_records = extra_num_records;
+  x.record_stride = extra_record_stride;
+  x.indptr = extra_indptr;
+  x.indices = extra_indices;
+  x.num_indices = extra_num_indices;
+  return sparse_fwd_impl(q, num_tokens, num_heads, q_stride_token, q_stride_head, kv_records, num_records,
+                         record_stride, kv_indptr, kv_indices, num_indices, softmax_scale, flags, out,
+                         out_stride_token, out_stride_head, lse, workspace, workspace_bytes, stream, x);
+}
+
 
 const char *mla_last_error(void) { return g_error; }
 
@@ -166,103 +332,6 @@ mla_status_t mla_workspace_reserve(int device, size_t bytes) {
   return workspace_get(device, bytes, &p);
 }
 
-mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
-                            int64_t q_stride_head, const void *kv_records, int64_t num_records, int64_t record_stride,
-                            const void *kv_indptr, const void *kv_indices, int64_t num_indices, float softmax_scale,
-                            uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head, float *lse,
-                            void *workspace, size_t workspace_bytes, void *stream) {
-  if (flags & ~kKnownFlags) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: unknown flag bits 0x%x", flags & ~kKnownFlags);
-  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_tokens %lld < 0", (long long)num_tokens);
-  if (num_tokens > INT32_MAX - 1) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_tokens %lld too large", (long long)num_tokens);
-  if (num_heads < 1 || num_heads > MLA_MAX_HEADS)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_heads %d outside 1..%d", num_heads, MLA_MAX_HEADS);
-  if (q_stride_token < 0 || q_stride_head < 0 || out_stride_token < 0 || out_stride_head < 0)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: negative stride");
-  if ((q_stride_token | q_stride_head) & 1)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q strides must be even (got %lld, %lld)", (long long)q_stride_token,
-                (long long)q_stride_head);
-  if ((out_stride_token | out_stride_head) & 1)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out strides must be even (got %lld, %lld)",
-                (long long)out_stride_token, (long long)out_stride_head);
-  if (record_stride != MLA_RECORD_BYTES)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
-                MLA_RECORD_BYTES);
-  if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_records %lld < 0", (long long)num_records);
-  if (num_records > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_records %lld >= 2^31", (long long)num_records);
-  if (num_indices < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: num_indices %lld < 0", (long long)num_indices);
-  if (num_indices >= MLA_MAX_INDICES)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_indices %lld >= 2^29", (long long)num_indices);
-  const bool i64 = (flags & MLA_FLAG_INDEX_I64) != 0;
-  const bool want_lse = (flags & MLA_FLAG_RETURN_LSE) != 0;
-  const uintptr_t idx_align = i64 ? 8 : 4;
-  if (!aligned(q, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: q base not 4-byte aligned");
-  if (!aligned(out, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out base not 4-byte aligned");
-  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: kv_records base not 16-byte aligned");
-  if (!aligned(kv_indptr, idx_align) || !aligned(kv_indices, idx_align))
-    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: index arrays not aligned to their element size");
-  if (want_lse && !aligned(lse, 4)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: lse not 4-byte aligned");
-  if ((flags & MLA_FLAG_CHUNK_MASK) && num_tokens > mla::kMaxSplitRows)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: forced split-KV serves at most %lld rows",
-                (long long)mla::kMaxSplitRows);
-  if (num_tokens == 0) return MLA_OK;
-  if (!q || !out || !kv_indptr) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL q, out or kv_indptr");
-  if (want_lse && !lse) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: MLA_FLAG_RETURN_LSE with lse == NULL");
-  if (num_indices > 0 && !kv_indices) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_indices");
-  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: NULL kv_records");
-
-  int device = -1;
-  if (hipGetDevice(&device) != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: hipGetDevice failed");
-  const bool forced = (flags & MLA_FLAG_CHUNK_MASK) != 0;
-  const int cus = forced ? 0 : device_cus(device);
-  if (!forced && cus <= 0) return fail(MLA_ERR_HIP, "mla_sparse_fwd: cannot query device %d", device);
-  int32_t forced_chunk = 0;
-  const int64_t bound = plan_split(num_tokens, num_indices, cus, flags, &forced_chunk);
-
-  if (bound > INT32_MAX)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: %lld chunks exceed the grid", (long long)bound);
-
-  mla::FwdArgs a;
-  a.q = static_cast<const uint16_t *>(q);
-  a.q_stride_token = q_stride_token;
-  a.q_stride_head = q_stride_head;
-  a.records = static_cast<const uint8_t *>(kv_records);
-  a.num_records = num_records;
-  a.indptr = kv_indptr;
-  a.indices = num_indices > 0 ? kv_indices : kv_indptr;  // element 0 may be read, never used
-  a.num_indices = num_indices;
-  a.index_i64 = i64;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.num_tokens = (int32_t)num_tokens;
-  a.num_heads = num_heads;
-  a.out = static_cast<uint16_t *>(out);
-  a.out_stride_token = out_stride_token;
-  a.out_stride_head = out_stride_head;
-  a.lse = want_lse ? lse : nullptr;
-  a.chunk_forced = forced_chunk;
-  a.chunk_bound = bound;
-  a.ws_out = nullptr;
-  a.ws_lse = nullptr;
-  a.ws_prefix = nullptr;
-  if (bound > 0) {
-    const mla::SplitLayout l = mla::split_layout(num_tokens, num_heads, bound);
-    void *ws = workspace;
-    if (ws) {
-      if (workspace_bytes < l.bytes)
-        return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.bytes);
-      if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace not 256-byte aligned");
-    } else {
-      mla_status_t st = workspace_get(device, l.bytes, &ws);
-      if (st != MLA_OK) return st;
-    }
-    char *base = static_cast<char *>(ws);
-    a.ws_out = reinterpret_cast<float *>(base + l.out_off);
-    a.ws_lse = reinterpret_cast<float *>(base + l.lse_off);
-    a.ws_prefix = reinterpret_cast<int32_t *>(base + l.prefix_off);
-  }
-  hipError_t e = mla::launch_sparse_fwd(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: launch failed: %s", hipGetErrorString(e));
-  return MLA_OK;
-}
 
 mla_status_t mla_cache_insert(const void *kv_c, int64_t kv_c_stride_token, const void *k_pe, int64_t k_pe_stride_token,
                               const int64_t *slot_mapping, int64_t num_tokens, void *kv_records, int64_t num_records,

@@ -30,6 +30,14 @@ struct FwdArgs {
   float *ws_out;       // [chunk_bound, H, 512] float32 partials
   float *ws_lse;       // [chunk_bound, H] float32 base-2 log-sum-exp
   int32_t *ws_prefix;  // [T + 1] first chunk of each row
+  // Optional second segment (extra_indptr != nullptr): a second pool whose
+  // CSR list joins each row's softmax.  Optional per-head sink logits.
+  const uint8_t *extra_records = nullptr;
+  int64_t extra_num_records = 0;
+  const void *extra_indptr = nullptr;
+  const void *extra_indices = nullptr;
+  int64_t extra_num_indices = 0;
+  const float *sink = nullptr;
 };
 
 hipError_t launch_sparse_fwd(const FwdArgs &a, hipStream_t stream);

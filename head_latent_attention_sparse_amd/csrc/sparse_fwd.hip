@@ -71,7 +71,29 @@ struct FwdKernelArgs {
   int32_t tokens;
   int32_t forced_chunk;  // split pass: chunk size if > 0, else chosen by split_plan
   int64_t bound;         // split pass: its workgroups, an upper bound on the chunks
+  // second segment (kExtra): its pool and CSR list
+  const uint8_t *erec;
+  int64_t enum_records;
+  const void *eindptr;
+  const void *eindices;
+  int64_t ennz;
+  const float *sink;  // [heads] sink logits (natural-log units of the scaled logits), or nullptr
 };
+
+// A workgroup's share of a row.  Entry v of the row (0 <= v < lenp + lene)
+// is primary entry beg + v for v < lenp, else extra entry ebeg + v - lenp;
+// the workgroup takes entries [vb, ve).
+struct RowRange {
+  int64_t t, beg, lenp, ebeg, vb, ve;
+};
+
+// Clamp a CSR pair to [0, nnz] (a decreasing pair gives an empty range).
+__device__ __forceinline__ void clamp_range(int64_t b, int64_t e, int64_t nnz, int64_t &beg, int64_t &len) {
+  b = b < 0 ? 0 : (b > nnz ? nnz : b);
+  e = e < b ? b : (e > nnz ? nnz : e);
+  beg = b;
+  len = e - b;
+}
 
 // ---- Split-KV plan, computed by every workgroup of the partial pass ----
 // The same plan in every workgroup (and no separate launch): row lengths
@@ -129,34 +151,49 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
 __device__ __forceinline__ int32_t wave_sum(int32_t v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
 struct SplitPlanLds {
-  uint32_t n[4];  // per wave: sum of lengths (exact for a non-decreasing indptr: < 2^29)
+  uint32_t n[4];  // per wave: sum of lengths (exact for non-decreasing CSR offsets: < 2^30)
   int32_t rows[4];
   int32_t cnt[kPlanCandidates][4];
   int32_t wave_tot[4];
-  int32_t hit[3];  // row, begin, end of this workgroup's chunk
+  int32_t hit[6];  // row, chunk begin, row length, primary begin, primary length, extra begin
 };
 
-template <typename IdxT>
-__device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t, int64_t &beg, int64_t &end) {
+template <typename IdxT, bool kExtra>
+__device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, RowRange &rr) {
   SplitPlanLds &sh = *reinterpret_cast<SplitPlanLds *>(scratch);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
   const int32_t tokens = p.tokens;
   const int32_t r0 = 2 * tid;
 
-  // rows r0 and r0 + 1: three offsets, one round trip
-  int32_t len[2] = {0, 0}, rb[2] = {0, 0};
+  // rows r0 and r0 + 1: three offsets per segment, one round trip.
+  // len = the row's entries over both segments (< 2^30).
+  int32_t len[2] = {0, 0}, rb[2] = {0, 0}, lp[2] = {0, 0}, eb[2] = {0, 0};
   if (r0 < tokens) {
-    const IdxT x0 = indptr[r0], x1 = indptr[r0 + 1], x2 = indptr[r0 + 1 < tokens ? r0 + 2 : r0 + 1];
-    __builtin_amdgcn_sched_barrier(0);  // all three loads in flight before any use
+    const int r2 = r0 + 1 < tokens ? r0 + 2 : r0 + 1;
+    const IdxT x0 = indptr[r0], x1 = indptr[r0 + 1], x2 = indptr[r2];
+    IdxT y0 = 0, y1 = 0, y2 = 0;
+    if (kExtra) {
+      const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
+      y0 = eindptr[r0];
+      y1 = eindptr[r0 + 1];
+      y2 = eindptr[r2];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before any use
     const int64_t xs[3] = {(int64_t)x0, (int64_t)x1, (int64_t)x2};
+    const int64_t ys[3] = {(int64_t)y0, (int64_t)y1, (int64_t)y2};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int64_t b = xs[i], e = xs[i + 1];
-      b = b < 0 ? 0 : (b > p.nnz ? p.nnz : b);
-      e = e < b ? b : (e > p.nnz ? p.nnz : e);
+      int64_t b, l;
+      clamp_range(xs[i], xs[i + 1], p.nnz, b, l);
       rb[i] = (int32_t)b;  // nnz < 2^29
-      len[i] = (int32_t)(e - b);
+      lp[i] = (int32_t)l;
+      len[i] = (int32_t)l;
+      if (kExtra) {
+        clamp_range(ys[i], ys[i + 1], p.ennz, b, l);
+        eb[i] = (int32_t)b;
+        len[i] += (int32_t)l;
+      }
     }
   }
 
@@ -209,21 +246,27 @@ __device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, int64_t &t,
     if (tid == 0) p.ws_prefix[tokens] = (int32_t)total;
   }
   const int64_t b = blockIdx.x;
-  if (r0 < tokens && f0 <= b && b < f1) {
-    sh.hit[0] = r0;
-    sh.hit[1] = rb[0] + (int32_t)(b - f0) * chunk;
-    sh.hit[2] = rb[0] + len[0];
-  } else if (r0 + 1 < tokens && f1 <= b && b < f2) {
-    sh.hit[0] = r0 + 1;
-    sh.hit[1] = rb[1] + (int32_t)(b - f1) * chunk;
-    sh.hit[2] = rb[1] + len[1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t fb = i == 0 ? f0 : f1, fe = i == 0 ? f1 : f2;
+    if (r0 + i < tokens && fb <= b && b < fe) {
+      sh.hit[0] = r0 + i;
+      sh.hit[1] = (int32_t)(b - fb) * chunk;
+      sh.hit[2] = len[i];
+      sh.hit[3] = rb[i];
+      sh.hit[4] = lp[i];
+      sh.hit[5] = eb[i];
+    }
   }
   __syncthreads();
   const bool has_work = b < total;
   if (has_work) {
-    t = sh.hit[0];
-    beg = sh.hit[1];
-    end = beg + chunk < sh.hit[2] ? beg + chunk : (int64_t)sh.hit[2];
+    rr.t = sh.hit[0];
+    rr.vb = sh.hit[1];
+    rr.ve = rr.vb + chunk < sh.hit[2] ? rr.vb + chunk : (int64_t)sh.hit[2];
+    rr.beg = sh.hit[3];
+    rr.lenp = sh.hit[4];
+    rr.ebeg = sh.hit[5];
   }
   __syncthreads();  // the scratch (the tile buffer) is reused next
   return has_work;
@@ -245,7 +288,7 @@ __device__ __forceinline__ floatx4_t qk_latent_tile(const uint8_t *krec, int g, 
   return acc;
 }
 
-template <typename IdxT, bool kSplit, bool kLse>
+template <typename IdxT, bool kSplit, bool kLse, bool kExtra>
 __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_rec[kTileKeys * kRecordBytes];
   __shared__ __attribute__((aligned(16))) float s_logit[16 * kLogitPitch];
@@ -258,38 +301,50 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   const int n = lane & 15;  // MFMA row/column index of this lane
   const int g = lane >> 4;  // MFMA k-group of this lane
 
-  // ---- this workgroup's CSR entries: a whole row, or a chunk of one
+  // ---- this workgroup's entries: a whole row, or a chunk of one
   const IdxT *indices = static_cast<const IdxT *>(p.indices);
-  int64_t t, beg, end;
+  const IdxT *eindices = static_cast<const IdxT *>(p.eindices);
+  RowRange rr;
   if (kSplit) {
-    if (!split_plan<IdxT>(p, s_rec, t, beg, end)) return;  // whole workgroup
+    if (!split_plan<IdxT, kExtra>(p, s_rec, rr)) return;  // whole workgroup
   } else {
     const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
-    t = blockIdx.x;
-    int64_t rb = (int64_t)indptr[t];
-    int64_t re = (int64_t)indptr[t + 1];
-    rb = rb < 0 ? 0 : (rb > p.nnz ? p.nnz : rb);
-    re = re < rb ? rb : (re > p.nnz ? p.nnz : re);
-    beg = rb;
-    end = re;
+    rr.t = blockIdx.x;
+    clamp_range((int64_t)indptr[rr.t], (int64_t)indptr[rr.t + 1], p.nnz, rr.beg, rr.lenp);
+    int64_t lene = 0;
+    rr.ebeg = 0;
+    if (kExtra) {
+      const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
+      clamp_range((int64_t)eindptr[rr.t], (int64_t)eindptr[rr.t + 1], p.ennz, rr.ebeg, lene);
+    }
+    rr.vb = 0;
+    rr.ve = rr.lenp + lene;
   }
-  const int ntiles = (int)((end - beg + kTileKeys - 1) / kTileKeys);
+  const int64_t t = rr.t;
+  const int ntiles = (int)((rr.ve - rr.vb + kTileKeys - 1) / kTileKeys);
 
   // Raw id of entry j of tile `tile`.  The load is unconditional (an entry
-  // past the end reads element 0 instead, which exists: with no indices the
-  // array is a placeholder that points at indptr) and its value is not looked
-  // at here, so it stays in flight until slot_of turns it into a slot, an
-  // iteration later for the index prefetch.
+  // past the end reads element 0 of the primary list instead, which exists:
+  // with no indices the array is a placeholder that points at indptr) and its
+  // value is not looked at here, so it stays in flight until slot_of turns it
+  // into a slot, an iteration later for the index prefetch.
   auto fetch_entry = [&](int tile, int j) -> IdxT {
-    const int64_t e = beg + (int64_t)tile * kTileKeys + j;
-    return indices[e < end ? e : 0];
+    const int64_t v = rr.vb + (int64_t)tile * kTileKeys + j;
+    if (!kExtra) return indices[v < rr.ve ? rr.beg + v : 0];
+    const IdxT *src = v < rr.lenp ? indices + (rr.beg + v) : eindices + (rr.ebeg + v - rr.lenp);
+    return *(v < rr.ve ? src : indices);
   };
-  // The slot entry j of tile `tile` names, or -1 (past the end, masked, or
-  // outside the pool).
+  // What entry j of tile `tile` names: a primary slot s as s, an extra-pool
+  // slot s as -2 - s, and -1 when it is past the end, masked, or outside its
+  // pool.  (Pools hold fewer than 2^31 - 2 records.)
   auto slot_of = [&](IdxT raw, int tile, int j) -> int {
     const int64_t x = (int64_t)raw;
-    const bool in_range = beg + (int64_t)tile * kTileKeys + j < end;
-    return (in_range && x >= 0 && x < p.num_records) ? (int)x : -1;
+    const int64_t v = rr.vb + (int64_t)tile * kTileKeys + j;
+    const bool in_range = v < rr.ve;
+    if (!kExtra) return (in_range && x >= 0 && x < p.num_records) ? (int)x : -1;
+    const bool extra = v >= rr.lenp;
+    const bool ok = in_range && x >= 0 && x < (extra ? p.enum_records : p.num_records);
+    return ok ? (extra ? -2 - (int)x : (int)x) : -1;
   };
 
   // Gather mapping: 4 threads per record; thread (rec, sub) moves the 16-byte
@@ -306,8 +361,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
 #pragma unroll
   for (int i = 0; i < kChunksPerThread; ++i) pf[i] = u32x4_t{0u, 0u, 0u, 0u};
   auto issue_gather_slot = [&](int slot) {
-    if (slot >= 0) {
-      const uint8_t *src = p.rec + (int64_t)slot * kRecordBytes + 16 * gsub;
+    if (kExtra ? slot != -1 : slot >= 0) {
+      const uint8_t *src = (slot >= 0 ? p.rec + (int64_t)slot * kRecordBytes
+                                      : p.erec + (int64_t)(-2 - slot) * kRecordBytes) + 16 * gsub;
 #pragma unroll
       for (int i = 0; i < kChunksPerThread - 1; ++i) pf[i] = *reinterpret_cast<const u32x4_t *>(src + 64 * i);
       if (gsub == 0) pf[kChunksPerThread - 1] = *reinterpret_cast<const u32x4_t *>(src + 64 * (kChunksPerThread - 1));
@@ -457,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       racc = mfma_16x16x32_bf16(as_bf16x8(qr[1]), as_bf16x8(r1), racc);
       sacc += racc;
     }
-    const bool valid = s_slot[buf][wave * 16 + n] >= 0;
+    const bool valid = kExtra ? s_slot[buf][wave * 16 + n] != -1 : s_slot[buf][wave * 16 + n] >= 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       s_logit[(4 * g + j) * kLogitPitch + wave * 16 + n] = valid ? sacc[j] * p.scale_log2 : -INFINITY;
@@ -558,7 +614,23 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // ---- epilogue: head n's total sum over the four k-groups
   float l_tot = l_run + xor_shuffle(l_run, 16);
   l_tot += xor_shuffle(l_tot, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  float o_scale = 1.f;  // applied to O with 1 / l
+  if (!kSplit && p.sink) {
+    // the sink: one more logit with a zero value (the split pass adds it in the merge)
+    const float s2 = p.sink[n < p.heads ? n : 0] * kLog2e;
+    if (m_run == -INFINITY) {
+      m_run = s2;
+      l_tot = s2 == -INFINITY ? 0.f : 1.f;
+      o_scale = 0.f;
+    } else if (s2 > m_run) {
+      o_scale = fast_exp2(m_run - s2);
+      l_tot = l_tot * o_scale + 1.f;
+      m_run = s2;
+    } else {
+      l_tot += fast_exp2(s2 - m_run);
+    }
+  }
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
   const bool empty = m_run == -INFINITY;
   if (n < p.heads) {
     if (!kSplit) {
@@ -581,9 +653,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   }
 }
 
-// Combine a row's chunk partials: lse = log2 sum_s 2^lse_s,
+// Combine a row's chunk partials: lse = log2 (sum_s 2^lse_s [+ 2^sink]),
 // out = sum_s 2^(lse_s - lse) o_s (an empty partial, lse_s = -inf, weighs 0;
-// no partial or all empty -> out 0, lse -inf).  One workgroup per (row,
+// the sink, when given, is one more term with a zero value; nothing at all
+// -> out 0, lse -inf).  One workgroup per (row,
 // head, 128-column quarter): 8 chunk lanes x 32 column quads accumulate and
 // reduce through LDS, so a row with many chunks is read by 256 threads.
 constexpr int kMergeThreads = 256;
@@ -606,7 +679,8 @@ __device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) 
 template <bool kLse>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse,
                                                               const int32_t *prefix, int32_t heads, uint16_t *out,
-                                                              int64_t o_st, int64_t o_sh, float *lse) {
+                                                              int64_t o_st, int64_t o_sh, float *lse,
+                                                              const float *sink) {
   __shared__ floatx4_t s_part[kMergeChunkLanes][32];
   __shared__ float s_red[kMergeThreads / 64];
   const int tid = threadIdx.x;
@@ -618,12 +692,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
   const int nc = prefix[t + 1] - (int)c0;
   const float *lp = ws_lse + c0 * heads + h;  // chunk s at lp[s * heads]
 
-  float mx = -INFINITY;
+  const float s2 = sink ? sink[h] * kLog2e : -INFINITY;
+  float mx = tid == 0 ? s2 : -INFINITY;
   for (int s = tid; s < nc; s += kMergeThreads) mx = fmaxf(mx, lp[(int64_t)s * heads]);
   mx = block_reduce(mx, s_red, true);
   float tot = 0.f;
-  if (mx != -INFINITY)
+  if (mx != -INFINITY) {
+    if (tid == 0) tot = fast_exp2(s2 - mx);
     for (int s = tid; s < nc; s += kMergeThreads) tot += fast_exp2(lp[(int64_t)s * heads] - mx);
+  }
   tot = block_reduce(tot, s_red, false);
 
   const int cl = tid >> 5;  // chunk lane
@@ -650,7 +727,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
   }
 }
 
-template <typename IdxT>
+template <typename IdxT, bool kExtra>
 hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   FwdKernelArgs k;
   k.q = a.q;
@@ -673,34 +750,42 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   k.tokens = a.num_tokens;
   k.forced_chunk = a.chunk_forced;
   k.bound = a.chunk_bound;
+  k.erec = a.extra_records;
+  k.enum_records = a.extra_num_records;
+  k.eindptr = a.extra_indptr;
+  k.eindices = a.extra_indices;
+  k.ennz = a.extra_num_indices;
+  k.sink = a.sink;
   const dim3 block(kThreads);
   const bool lse = a.lse != nullptr;
   if (a.chunk_bound <= 0) {
     const dim3 grid((unsigned)a.num_tokens);
     if (lse)
-      sparse_fwd_kernel<IdxT, false, true><<<grid, block, 0, stream>>>(k);
+      sparse_fwd_kernel<IdxT, false, true, kExtra><<<grid, block, 0, stream>>>(k);
     else
-      sparse_fwd_kernel<IdxT, false, false><<<grid, block, 0, stream>>>(k);
+      sparse_fwd_kernel<IdxT, false, false, kExtra><<<grid, block, 0, stream>>>(k);
     return hipGetLastError();
   }
   hipError_t e;
-  sparse_fwd_kernel<IdxT, true, false><<<dim3((unsigned)a.chunk_bound), block, 0, stream>>>(k);
+  sparse_fwd_kernel<IdxT, true, false, kExtra><<<dim3((unsigned)a.chunk_bound), block, 0, stream>>>(k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * 4));
   if (lse)
     merge_kernel<true><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                           a.out_stride_token, a.out_stride_head, a.lse);
+                                                           a.out_stride_token, a.out_stride_head, a.lse, a.sink);
   else
     merge_kernel<false><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                            a.out_stride_token, a.out_stride_head, nullptr);
+                                                            a.out_stride_token, a.out_stride_head, nullptr, a.sink);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_sparse_fwd(const FwdArgs &a, hipStream_t stream) {
-  return a.index_i64 ? launch_typed<int64_t>(a, stream) : launch_typed<int32_t>(a, stream);
+  const bool extra = a.extra_indptr != nullptr;
+  if (a.index_i64) return extra ? launch_typed<int64_t, true>(a, stream) : launch_typed<int64_t, false>(a, stream);
+  return extra ? launch_typed<int32_t, true>(a, stream) : launch_typed<int32_t, false>(a, stream);
 }
 
 }  // namespace mla

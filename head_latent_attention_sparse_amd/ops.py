@@ -41,6 +41,8 @@ _I64, _I32, _U32, _F32, _P, _SZ = (ctypes.c_int64, ctypes.c_int32, ctypes.c_uint
 SIGNATURES = {
     "mla_sparse_fwd": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P, _I64, _I64,
                               _P, _P, _SZ, _P]),
+    "mla_sparse_fwd_ex": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _P, _P,
+                                 _I64, _F32, _U32, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "mla_sparse_fwd_split_workgroups": (_I64, [_I64, _I64, _I32, _U32]),
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
@@ -128,15 +130,19 @@ def split_workgroups(num_tokens, num_indices, num_cus, chunk_tiles=0):
 
 
 def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid=False, out=None,
-               return_lse=False, chunk_tiles=0, workspace=None):
+               return_lse=False, chunk_tiles=0, workspace=None, attn_sink=None, extra_kv=None,
+               extra_indptr=None, extra_indices=None):
     """Sparse MLA forward over fp8_ds_mla records -> (out, lse or None).
 
     q [T, H, 576] bf16 (H <= 16, stride(2) == 1); kv_cache a record pool
     view; kv_indptr [T + 1] and kv_indices [nnz] int32 or int64 (the same
     dtype, contiguous); out optional [T, H, >= 512] bf16.  ``chunk_tiles``
     forces split-KV with chunks of that many 64-key tiles (0 = the library's
-    plan).  ``workspace``
-    optionally supplies the split partial buffer (a CUDA uint8 tensor).
+    plan).  ``workspace`` optionally supplies the split partial buffer (a
+    CUDA uint8 tensor).  ``attn_sink`` (float32 [H]) adds a per-head sink
+    logit; ``extra_kv`` / ``extra_indptr`` / ``extra_indices`` give a second
+    record pool and CSR list attended jointly with the first
+    (mla_sparse_fwd_ex).
     """
     if not (torch.is_tensor(q) and q.is_cuda and q.ndim == 3 and q.dtype == torch.bfloat16):
         raise ValueError("q must be a CUDA bf16 tensor [T, H, 576]")
@@ -154,6 +160,23 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
         raise ValueError("kv_indptr and kv_indices must have the same dtype")
     if kv_indptr.numel() != t_count + 1:
         raise ValueError("kv_indptr must have T + 1 entries")
+    use_extra = extra_indptr is not None or extra_indices is not None or extra_kv is not None
+    if use_extra:
+        if extra_kv is None or extra_indptr is None or extra_indices is None:
+            raise ValueError("extra_kv, extra_indptr and extra_indices come together")
+        for name, x in (("extra_indptr", extra_indptr), ("extra_indices", extra_indices)):
+            if not (torch.is_tensor(x) and x.device == q.device and x.ndim == 1 and x.is_contiguous()
+                    and x.dtype == kv_indices.dtype):
+                raise ValueError(f"{name} must be a contiguous 1-D tensor of kv_indices' dtype on q's device")
+        if extra_indptr.numel() != t_count + 1:
+            raise ValueError("extra_indptr must have T + 1 entries")
+        if not (torch.is_tensor(extra_kv) and extra_kv.device == q.device):
+            raise ValueError("extra_kv must be on q's device")
+        ekv_ptr, en_rec, epitch = _kv_rows(extra_kv)
+    if attn_sink is not None and not (torch.is_tensor(attn_sink) and attn_sink.dtype == torch.float32
+                                      and attn_sink.device == q.device and attn_sink.ndim == 1
+                                      and attn_sink.numel() == heads and attn_sink.is_contiguous()):
+        raise ValueError("attn_sink must be a contiguous float32 [H] tensor on q's device")
     if not (torch.is_tensor(kv_cache) and kv_cache.device == q.device):
         raise ValueError("kv cache must be on q's device")
     kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
@@ -175,8 +198,9 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
     with torch.cuda.device(dev):
         ws_ptr, ws_bytes = None, 0
+        total_nnz = kv_indices.numel() + (extra_indices.numel() if use_extra else 0)
         if t_count > 0:
-            need = L.mla_sparse_fwd_workspace_size(t_count, heads, kv_indices.numel(), flags, dev)
+            need = L.mla_sparse_fwd_workspace_size(t_count, heads, total_nnz, flags, dev)
             if need == ctypes.c_size_t(-1).value:
                 _check(3)
             if need > 0:
@@ -185,14 +209,29 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
                 if workspace.numel() < need:
                     raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
                 ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-        st = L.mla_sparse_fwd(
-            q.data_ptr(), t_count, heads, q.stride(0), q.stride(1),
-            kv_ptr, n_rec, pitch,
-            kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None, kv_indices.numel(),
-            float(softmax_scale), flags,
-            out.data_ptr(), out.stride(0), out.stride(1),
-            lse.data_ptr() if lse is not None else None,
-            ws_ptr, ws_bytes, _stream(q.device))
+        if use_extra or attn_sink is not None:
+            st = L.mla_sparse_fwd_ex(
+                q.data_ptr(), t_count, heads, q.stride(0), q.stride(1),
+                kv_ptr, n_rec, pitch,
+                kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None, kv_indices.numel(),
+                attn_sink.data_ptr() if attn_sink is not None else None,
+                ekv_ptr if use_extra else None, en_rec if use_extra else 0, epitch if use_extra else RECORD_BYTES,
+                extra_indptr.data_ptr() if use_extra else None,
+                extra_indices.data_ptr() if use_extra and extra_indices.numel() else None,
+                extra_indices.numel() if use_extra else 0,
+                float(softmax_scale), flags,
+                out.data_ptr(), out.stride(0), out.stride(1),
+                lse.data_ptr() if lse is not None else None,
+                ws_ptr, ws_bytes, _stream(q.device))
+        else:
+            st = L.mla_sparse_fwd(
+                q.data_ptr(), t_count, heads, q.stride(0), q.stride(1),
+                kv_ptr, n_rec, pitch,
+                kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None, kv_indices.numel(),
+                float(softmax_scale), flags,
+                out.data_ptr(), out.stride(0), out.stride(1),
+                lse.data_ptr() if lse is not None else None,
+                ws_ptr, ws_bytes, _stream(q.device))
     _check(st)
     return out, lse
 

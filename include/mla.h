@@ -119,6 +119,39 @@ mla_status_t mla_sparse_fwd(const void *q, int64_t num_tokens, int32_t num_heads
                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mla_sparse_fwd_ex - mla_sparse_fwd with an attention sink and a second KV
+ * segment, the attn_sink and extra_kv / extra_indptr / extra_indices
+ * arguments of sparse_mla_fwd that the flydsl_sparse_mla page lists (in the
+ * flydsl_sparse_mla_fp8ds_supported docstring) without defining them.
+ * Reading taken:
+ *   - attn_sink: float32 [num_heads] or NULL; head h gets one more logit
+ *     attn_sink[h] (natural-log units, compared with softmax_scale * q.k)
+ *     whose value vector is zero, so
+ *         out = sum_j e^{z_j} v_j / (e^{s_h} + sum_j e^{z_j}),
+ *         lse = ln(e^{s_h} + sum_j e^{z_j});
+ *     a row with no key then gives out 0 and lse = s_h; s_h = -inf is no sink.
+ *   - extra segment (extra_indptr != NULL): a second pool of fp8_ds_mla
+ *     records with its own CSR list; row t attends its primary entries and
+ *     extra_indices[extra_indptr[t] .. extra_indptr[t+1]) of the second
+ *     pool in one softmax (entries < 0 or >= extra_num_records masked).
+ *     Same index dtype as the primary list; extra_record_stride must be
+ *     656; extra_num_records < 2^31 - 2; num_indices + extra_num_indices
+ *     < 2^29.  With MLA_FLAG_CHUNK_TILES or the library's split plan, the
+ *     chunks run over both lists of a row; for the workspace size and the
+ *     split plan pass num_indices + extra_num_indices as num_indices.
+ * Every other argument is as for mla_sparse_fwd.  With attn_sink and
+ * extra_indptr both NULL this is mla_sparse_fwd.
+ */
+mla_status_t mla_sparse_fwd_ex(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                               int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                               int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                               int64_t num_indices, const float *attn_sink, const void *extra_records,
+                               int64_t extra_num_records, int64_t extra_record_stride, const void *extra_indptr,
+                               const void *extra_indices, int64_t extra_num_indices, float softmax_scale,
+                               uint32_t flags, void *out, int64_t out_stride_token, int64_t out_stride_head,
+                               float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mla_sparse_fwd_split_workgroups - the split-KV plan mla_sparse_fwd uses
  * (host only, no device access): 0 = one workgroup per row; otherwise the
  * number of workgroups of the partial pass, an upper bound on the number of
@@ -296,7 +329,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

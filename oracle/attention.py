@@ -17,7 +17,15 @@ Readings where the pages are silent (listed in the design doc):
 * a slot listed twice in a row counts twice (the softmax is a plain sum
   over the list);
 * the scale is used as the float32 the caller's float becomes at the
-  C boundary.
+  C boundary;
+* ``attn_sink`` and the ``extra_*`` segment (arguments of ``sparse_mla_fwd``
+  that the page's ``..._supported`` docstring lists but does not define):
+  the sink of head h is one more logit s_h, in the units of the scaled
+  logits, with a zero value vector, so it adds exp(s_h) to the softmax
+  denominator and to the LSE (an otherwise empty row gives out 0 and
+  lse = s_h); the extra segment is a second record pool with its own CSR
+  list whose keys join the row's softmax with the primary ones (masked by
+  the same rules against its own pool).
 """
 
 import numpy as np
@@ -25,7 +33,7 @@ import numpy as np
 from .records import bf16_bits_to_f32, decode_records
 
 
-def sparse_fwd(q_bits, records, indptr, indices, softmax_scale, rows=None):
+def sparse_fwd(q_bits, records, indptr, indices, softmax_scale, rows=None, extra=None, sink=None):
     """Reference forward.
 
     q_bits:  uint16 [T, H, 576] bf16 bit patterns of the absorbed query
@@ -34,29 +42,53 @@ def sparse_fwd(q_bits, records, indptr, indices, softmax_scale, rows=None):
     indptr:  int [T + 1] CSR offsets into ``indices``.
     indices: int [nnz] flat slot ids (negative = masked).
     rows:    optional iterable of row ids to compute (default: all).
+    extra:   optional (records2 uint8 [N2, 656], indptr2 [T + 1], indices2):
+             a second segment attended jointly with the first.
+    sink:    optional float [H] per-head sink logits (natural-log units of
+             the scaled logits), taken as the float32 values given.
     Returns (out float64 [R, H, 512], lse float64 [R, H]) for the R rows.
     """
     q = bf16_bits_to_f32(q_bits).astype(np.float64)  # exact
-    records = np.asarray(records, dtype=np.uint8)
-    indptr = np.asarray(indptr, dtype=np.int64)
-    indices = np.asarray(indices, dtype=np.int64)
-    n_records = records.shape[0]
+    segs = [(np.asarray(records, dtype=np.uint8), np.asarray(indptr, dtype=np.int64),
+             np.asarray(indices, dtype=np.int64))]
+    if extra is not None:
+        segs.append((np.asarray(extra[0], dtype=np.uint8), np.asarray(extra[1], dtype=np.int64),
+                     np.asarray(extra[2], dtype=np.int64)))
     sigma = np.float64(np.float32(softmax_scale))
     t_count, heads, _ = q.shape
     rows = range(t_count) if rows is None else list(rows)
+    s_logit = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
 
     out = np.zeros((len(rows), heads, 512), dtype=np.float64)
     lse = np.full((len(rows), heads), -np.inf, dtype=np.float64)
     for r, t in enumerate(rows):
-        ids = indices[indptr[t] : indptr[t + 1]]
-        ids = ids[(ids >= 0) & (ids < n_records)]
-        if ids.size == 0:
+        ks, vs = [], []
+        for recs, iptr, idx in segs:
+            ids = idx[iptr[t] : iptr[t + 1]]
+            ids = ids[(ids >= 0) & (ids < recs.shape[0])]
+            if ids.size:
+                k, v = decode_records(recs[ids])  # [n, 576], [n, 512]
+                ks.append(k)
+                vs.append(v)
+        if ks:
+            k, v = np.concatenate(ks), np.concatenate(vs)
+            z = sigma * (k @ q[t].T)  # [n, H] logits
+        else:
+            k, v = np.zeros((0, 576)), np.zeros((0, 512))
+            z = np.zeros((0, heads))
+        if s_logit is not None:  # the sink: one more logit per head, value 0
+            z = np.concatenate([z, s_logit[None, :]])
+            v = np.concatenate([v, np.zeros((1, 512))])
+        if z.shape[0] == 0:
             continue  # out 0, lse -inf
-        k, v = decode_records(records[ids])  # [n, 576], [n, 512]
-        z = sigma * (k @ q[t].T)  # [n, H] logits
         m = z.max(axis=0)
-        lse[r] = m + np.log(np.sum(np.exp(z - m), axis=0))
-        p = np.exp(z - lse[r])  # softmax weights, columns sum to 1
+        if np.all(np.isneginf(m)):
+            continue
+        dead = np.isneginf(m)  # a head with no key and a -inf sink: out 0, lse -inf
+        m_safe = np.where(dead, 0.0, m)
+        total = np.sum(np.exp(z - m_safe), axis=0)
+        lse[r] = np.where(dead, -np.inf, m_safe + np.log(np.where(dead, 1.0, total)))
+        p = np.where(dead, 0.0, np.exp(z - np.where(dead, 0.0, lse[r])))  # softmax weights, columns sum to 1
         out[r] = p.T @ v
     return out, lse
 

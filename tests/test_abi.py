@@ -267,3 +267,35 @@ def test_v_up_proj_rejections(kw, status):
 def test_v_up_proj_zero_tokens_is_a_no_op():
     st, _ = vproj(T=0, lat=None, w=None, out=None)
     assert st == OK
+
+
+def fwd_ex(**kw):
+    args = dict(q=A, T=4, H=16, qst=16 * 576, qsh=576, kv=A, n=100, pitch=656, indptr=A, indices=A, nnz=10,
+                sink=None, erec=A, en=50, epitch=656, eptr=A, eidx=A, ennz=10, scale=1.0, flags=2, out=A,
+                ost=16 * 512, osh=512, lse=A, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_sparse_fwd_ex(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(epitch=672), UNSUPPORTED),
+    (dict(en=-1), INVALID),
+    (dict(en=(1 << 31) - 2), UNSUPPORTED),
+    (dict(ennz=(1 << 29) - 10), UNSUPPORTED),   # both lists together reach 2^29
+    (dict(erec=A + 8), UNSUPPORTED),
+    (dict(eptr=A + 2), INVALID),
+    (dict(eidx=None), INVALID),
+    (dict(sink=A + 2), INVALID),
+    (dict(H=17), UNSUPPORTED),
+])
+def test_fwd_ex_rejections(kw, status):
+    st, msg = fwd_ex(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_fwd_ex_zero_tokens_is_a_no_op():
+    st, _ = fwd_ex(T=0, q=None, out=None, indptr=None, indices=None, lse=None)
+    assert st == OK

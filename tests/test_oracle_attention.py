@@ -194,3 +194,71 @@ def test_merge_all_empty_partials():
     l = np.full(2, -np.inf)
     out, lse = merge_partials([o, o, o], [l, l, l])
     assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ---- the sink and the second segment (readings: a sink is one more logit
+# with a zero value; the extra segment's keys join the same softmax)
+
+def bits_of(x):
+    return bf16_bits(torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def _records(rng, n):
+    return encode_records(bits_of(rng.standard_normal((n, 512))), bits_of(rng.standard_normal((n, 64))))
+
+
+def _small_problem(seed, t=5, h=3, n=40, n2=30):
+    rng = np.random.default_rng(seed)
+    q = bits_of(rng.standard_normal((t, h, 576)))
+    rec = _records(rng, n)
+    rec2 = _records(rng, n2)
+    lens = rng.integers(0, 9, t)
+    lens[1] = 0
+    indptr = np.concatenate([[0], np.cumsum(lens)])
+    indices = rng.integers(-2, n + 3, indptr[-1])
+    lens2 = rng.integers(0, 7, t)
+    lens2[2] = 0
+    indptr2 = np.concatenate([[0], np.cumsum(lens2)])
+    indices2 = rng.integers(-2, n2 + 3, indptr2[-1])
+    return q, rec, indptr, indices, rec2, indptr2, indices2
+
+
+def test_extra_segment_is_one_pool_with_both_lists():
+    q, rec, ip, ix, rec2, ip2, ix2 = _small_problem(11)
+    got_out, got_lse = sparse_fwd(q, rec, ip, ix, 0.07, extra=(rec2, ip2, ix2))
+    # the same attention over one pool holding both: extra slot s -> N + s
+    pool = np.concatenate([rec, rec2])
+    n = rec.shape[0]
+    rows = []
+    for t in range(q.shape[0]):
+        a = ix[ip[t]:ip[t + 1]]
+        a = np.where((a >= 0) & (a < n), a, -1)
+        b = ix2[ip2[t]:ip2[t + 1]]
+        b = np.where((b >= 0) & (b < rec2.shape[0]), b + n, -1)
+        rows.append(np.concatenate([a, b]))
+    ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    want_out, want_lse = sparse_fwd(q, pool, ptr, np.concatenate(rows), 0.07)
+    np.testing.assert_allclose(got_out, want_out, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(got_lse), np.isneginf(want_lse))
+    fin = np.isfinite(want_lse)
+    np.testing.assert_allclose(got_lse[fin], want_lse[fin], rtol=0, atol=1e-12)
+
+
+def test_sink_closed_form():
+    q, rec, ip, ix, rec2, ip2, ix2 = _small_problem(12)
+    sink = np.array([0.5, -3.0, 2.25], dtype=np.float32)
+    base_out, base_lse = sparse_fwd(q, rec, ip, ix, 0.07, extra=(rec2, ip2, ix2))
+    out, lse = sparse_fwd(q, rec, ip, ix, 0.07, extra=(rec2, ip2, ix2), sink=sink)
+    want_lse = np.logaddexp(base_lse, sink.astype(np.float64)[None, :])
+    np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-12)
+    w = np.exp(np.where(np.isneginf(base_lse), -np.inf, base_lse - want_lse))
+    np.testing.assert_allclose(out, base_out * w[..., None], rtol=0, atol=1e-12)
+    # row 1 has no primary keys; where it has no extra keys either, lse = sink and out = 0
+    empty = [t for t in range(q.shape[0]) if np.isneginf(base_lse[t, 0])]
+    for t in empty:
+        np.testing.assert_array_equal(lse[t], sink.astype(np.float64))
+        assert np.all(out[t] == 0)
+    # a -inf sink is no sink
+    out_n, lse_n = sparse_fwd(q, rec, ip, ix, 0.07, extra=(rec2, ip2, ix2), sink=np.full(3, -np.inf, np.float32))
+    np.testing.assert_array_equal(out_n, base_out)
+    np.testing.assert_array_equal(lse_n, base_lse)
