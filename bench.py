@@ -53,6 +53,9 @@ def parse():
                     help="measure the decode epilogue (query concat + RoPE + insert) instead of the forward")
     ap.add_argument("--gather", action="store_true",
                     help="measure the context gather + upconvert to bf16 instead of the forward")
+    ap.add_argument("--with-sink-extra", action="store_true",
+                    help="forward variant: add per-head sink logits and a second segment of 256 entries per row "
+                         "over a second 16384-record pool (mla_sparse_fwd_ex)")
     ap.add_argument("--vproj", action="store_true",
                     help="measure the W_UV up-projection with the sigmoid gate instead of the forward")
     return ap.parse_args()
@@ -103,6 +106,15 @@ def main():
     for b in w.setup_inserts:
         mla.cache_insert(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev), view)
     step_inserts = [(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev)) for b in w.step_inserts]
+    ex = {}
+    if args.with_sink_extra:
+        seg = workloads.extra_segment(t_count, heads)
+        pool2 = torch.zeros((seg.num_records, 656), dtype=torch.uint8, device=dev)
+        mla.cache_insert(seg.insert.kv_c.to(dev), seg.insert.k_pe.to(dev), seg.insert.slots.to(dev), pool2)
+        ex = dict(attn_sink=seg.sink.to(dev), extra_kv=pool2, extra_indptr=seg.indptr.to(dev),
+                  extra_indices=seg.indices.to(dev))
+        nnz += int(seg.indices.numel())
+        nnz_valid += int(seg.indices.numel())
     q = w.q.to(dev)
     indptr, indices = w.indptr.to(dev), w.indices.to(dev)
     out = torch.empty((t_count, heads, 512), dtype=torch.bfloat16, device=dev)
@@ -124,7 +136,7 @@ def main():
         for kv_c, k_pe, slots in step_inserts:
             mla.cache_insert(kv_c, k_pe, slots, view)
         return mla.sparse_fwd(q, view, indptr, indices, w.softmax_scale, has_invalid=w.has_invalid,
-                              out=out, return_lse=w.return_lse, workspace=workspace)
+                              out=out, return_lse=w.return_lse, workspace=workspace, **ex)
 
     log("inputs resident; warmup")
     for _ in range(args.warmup):
@@ -158,7 +170,7 @@ def main():
     achieved_gbps = gathered / (dev_ms * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE) and args.config == 3:
+    if os.path.exists(TRAFFIC_FILE) and args.config == 3 and not args.with_sink_extra:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha256_16") == source_hash():
@@ -178,7 +190,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.config],
+            "workload": WORKLOAD_NAMES[args.config] + (
+                "; + per-head sink and a second segment of 256 slots/row over 16384 more records"
+                if args.with_sink_extra else ""),
             "rows": t_count,
             "heads": heads,
             "records": w.num_records,
@@ -206,7 +220,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {dev_ms:.3f} ms)")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, seg if args.with_sink_extra else None)
     print(json.dumps(result), flush=True)
 
 
@@ -425,8 +439,9 @@ def bench_vproj(args, dev):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, target_seconds):
-    """The fp64 oracle on a bounded sample of the same workload's rows."""
+def cpu_baseline(w, target_seconds, seg=None):
+    """The fp64 oracle on a bounded sample of the same workload's rows (with
+    the sink and second segment when `seg` is given)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -445,15 +460,23 @@ def cpu_baseline(w, target_seconds):
             recs = [encode_records(kv[i:i + 8192], pe[i:i + 8192]) for i in range(0, kv.shape[0], 8192)]
             pool[slots[keep]] = np.concatenate(recs)
         q_bits = bf16_bits(w.q)
+        extra, sink, eptr = None, None, None
+        if seg is not None:
+            eptr = seg.indptr.numpy().astype(np.int64)
+            pool2 = encode_records(bf16_bits(seg.insert.kv_c), bf16_bits(seg.insert.k_pe))  # slots 0..N2-1 in order
+            extra = (pool2, eptr, seg.indices.numpy().astype(np.int64))
+            sink = seg.sink.numpy()
         log("oracle records written; timing the oracle forward")
         rows, pairs, elapsed, t = [], 0, 0.0, 0
         # rows in order until the target CPU time is reached
         while t < w.num_tokens and elapsed < target_seconds:
             batch = list(range(t, min(t + 8, w.num_tokens)))
             t0 = time.perf_counter()
-            sparse_fwd(q_bits, pool, indptr, indices, w.softmax_scale, rows=batch)
+            sparse_fwd(q_bits, pool, indptr, indices, w.softmax_scale, rows=batch, extra=extra, sink=sink)
             elapsed += time.perf_counter() - t0
             pairs += int(indptr[batch[-1] + 1] - indptr[batch[0]])
+            if eptr is not None:
+                pairs += int(eptr[batch[-1] + 1] - eptr[batch[0]])
             rows.extend(batch)
             t += len(batch)
     return {

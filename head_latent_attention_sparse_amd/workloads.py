@@ -287,6 +287,29 @@ def v_up_proj_inputs(tokens: int = 4096, heads: int = 16, seed_offset: int = 8) 
     return VUpProjBatch(latent, w_uv, gate)
 
 
+@dataclass
+class ExtraSegment:
+    """A second record pool with its own CSR list, and per-head sink logits."""
+    insert: InsertBatch         # fills the second pool from zero bytes
+    num_records: int
+    indptr: torch.Tensor        # int32 [T + 1]
+    indices: torch.Tensor       # int32 [T * per_row]
+    sink: torch.Tensor          # float32 [H]
+
+
+def extra_segment(tokens: int, heads: int, per_row: int = 256, records: int = 16384,
+                  seed_offset: int = 9) -> ExtraSegment:
+    """For the sink / second-segment variant of a workload: a second pool of
+    `records` records (latent and rope N(0,1)), `per_row` distinct random
+    slots of it per row, and sink logits N(0,1)."""
+    g = torch.Generator().manual_seed(SEED_BASE + seed_offset)
+    fill = _pool_fill(g, records)
+    rows = [torch.randperm(records, generator=g)[:per_row] for _ in range(tokens)]
+    indptr, indices = _csr(rows)
+    sink = torch.randn((heads,), generator=g, dtype=torch.float32)
+    return ExtraSegment(fill, records, indptr, indices, sink)
+
+
 CONFIGS = {
     1: tiny,
     2: paged_decode,

@@ -129,3 +129,40 @@ def test_binding_rejections():
         mla.sparse_fwd(q, kv, ip, ix, 1.0, extra_kv=kv, extra_indptr=ip, extra_indices=ix.to(torch.int64))
     with pytest.raises(ValueError):
         mla.sparse_fwd(q, kv, ip, ix, 1.0, attn_sink=torch.zeros(3, device=DEV))
+
+
+def test_sparse_prefill_full_with_sink_and_extra_sampled():
+    """The measured variant (bench.py --with-sink-extra): the sparse prefill
+    workload at full size plus sinks and a 256-slot second segment per row;
+    sampled rows against the oracle, properties on all rows."""
+    from head_latent_attention_sparse_amd import workloads
+    from tests.helpers import oracle_subpool, remap_rows
+
+    say("fwd_ex sparse prefill full + sink + extra, sampled rows")
+    w = workloads.sparse_prefill()
+    seg = workloads.extra_segment(w.num_tokens, w.num_heads)
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=DEV)
+    for b in w.setup_inserts:
+        mla.cache_insert(b.kv_c.to(DEV), b.k_pe.to(DEV), b.slots.to(DEV), pool)
+    pool2 = torch.zeros((seg.num_records, 656), dtype=torch.uint8, device=DEV)
+    mla.cache_insert(seg.insert.kv_c.to(DEV), seg.insert.k_pe.to(DEV), seg.insert.slots.to(DEV), pool2)
+    out, lse = mla.sparse_fwd(w.q.to(DEV), pool, w.indptr.to(DEV), w.indices.to(DEV), w.softmax_scale,
+                              has_invalid=True, return_lse=True, attn_sink=seg.sink.to(DEV), extra_kv=pool2,
+                              extra_indptr=seg.indptr.to(DEV), extra_indices=seg.indices.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()  # every row has extra keys
+    rec2 = encode_records(bf16_bits(seg.insert.kv_c), bf16_bits(seg.insert.k_pe))
+    assert np.array_equal(pool2.cpu().numpy(), rec2), "second pool differs from the oracle writer"
+    indptr, indices = w.indptr.numpy(), w.indices.numpy()
+    empty = [t for t in range(w.num_tokens) if np.all(indices[indptr[t]:indptr[t + 1]] < 0)]
+    rows = sorted(set([0, 1, 2047, 4095] + empty[:2]))
+    needed = np.concatenate([indices[indptr[t]:indptr[t + 1]] for t in rows])
+    uniq, sub = oracle_subpool(w.num_records, w.setup_inserts, needed)
+    ptr, ind = remap_rows(indptr, indices, rows, uniq, w.num_records)
+    eptr_full, eind_full = seg.indptr.numpy().astype(np.int64), seg.indices.numpy().astype(np.int64)
+    eptr = np.concatenate([[0], np.cumsum([eptr_full[t + 1] - eptr_full[t] for t in rows])])
+    eind = np.concatenate([eind_full[eptr_full[t]:eptr_full[t + 1]] for t in rows])
+    ref_out, ref_lse = oracle_fwd(bf16_bits(w.q)[rows], sub, ptr, ind, w.softmax_scale,
+                                  extra=(rec2, eptr, eind), sink=seg.sink.numpy())
+    sel = torch.tensor(rows, dtype=torch.long, device=DEV)
+    assert_fwd_close(out[sel], lse[sel], ref_out, ref_lse, "prefill+sink+extra")
