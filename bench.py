@@ -1,7 +1,8 @@
 """Benchmark of the sparse MLA forward on MI355X (one GPU).
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                [--no-cpu-baseline] [--copy-calibration] [--epilogue | --gather | --vproj]
+                [--no-cpu-baseline] [--copy-calibration]
+                [--epilogue | --prefill-epilogue | --gather | --vproj | --with-sink-extra]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
@@ -51,6 +52,8 @@ def parse():
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--epilogue", action="store_true",
                     help="measure the decode epilogue (query concat + RoPE + insert) instead of the forward")
+    ap.add_argument("--prefill-epilogue", action="store_true",
+                    help="measure the prefill epilogue (q RoPE + key concat + insert) instead of the forward")
     ap.add_argument("--gather", action="store_true",
                     help="measure the context gather + upconvert to bf16 instead of the forward")
     ap.add_argument("--with-sink-extra", action="store_true",
@@ -88,6 +91,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.epilogue:
         bench_epilogue(args, dev)
+        return
+    if args.prefill_epilogue:
+        bench_prefill_epilogue(args, dev)
         return
     if args.gather:
         bench_gather(args, dev)
@@ -307,6 +313,70 @@ def bench_epilogue(args, dev):
             el = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": b / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the whole call ({b} tokens), numpy oracle, one thread, {el:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill_epilogue(args, dev):
+    """One prefill epilogue per step: RoPE on q's rope part in place, the full
+    key [k_nope | RoPE(k_pe)] for 16 heads, and the insert, 4096 tokens."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    log("generating the prefill epilogue inputs")
+    w = workloads.prefill_epilogue()
+    tp, h, nope = w.k_nope.shape
+    q, kn, kv, kp = w.q.to(dev), w.k_nope.to(dev), w.kv_c.to(dev), w.k_pe.to(dev)
+    slots, pos, table = w.slots.to(dev), w.positions.to(dev), w.cos_sin_cache.to(dev)
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=dev)
+    k_out = torch.empty((tp, h, nope + 64), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():  # q is rotated again each step: same traffic, values drift (not checked here)
+        mla.key_concat_insert(q, kn, kp, kv, pool, slots, positions=pos, cos_sin_cache=table, k_out=k_out)
+
+    ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
+    kept = int(((w.slots >= 0) & (w.slots < w.num_records)).sum())
+    read = tp * (h * 64 * 2 + h * nope * 2 + 512 * 2 + 64 * 2 + 8 + 8 + 64 * 4)
+    written = tp * (h * 64 * 2 + h * (nope + 64) * 2) + kept * 656
+    achieved = (read + written) / (dev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "MLA prefill epilogue (q RoPE + full-key concat + fp8_ds_mla insert): tokens/s",
+        "value": tp / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill epilogue: Tp={tp} tokens, H={h}, qk_nope {nope} + rope 64, RoPE, "
+                               f"{w.num_records} records, 5% slots skipped", "parallelism": "single GPU"},
+        "device_ms_per_step": dev_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": read + written},
+    }
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import key_concat_insert
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        bits = [bf16_bits(x) for x in (w.q, w.k_nope, w.kv_c, w.k_pe)]
+        opool = np.zeros((w.num_records, 656), dtype=np.uint8)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            key_concat_insert(*bits, w.slots.numpy(), opool, w.positions.numpy(), w.cos_sin_cache.numpy())
+            el = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": tp / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole call ({tp} tokens), numpy oracle, one thread, {el:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -18,6 +18,7 @@ from .ops import (  # noqa: F401
     cache_insert,
     decode_q_concat_insert,
     gather_upconvert,
+    key_concat_insert,
     lib,
     split_workgroups,
     sparse_fwd,

@@ -1,6 +1,11 @@
-// MLA decode epilogue for gfx950: the latent decode query
-// mqa_q = [ql_nope | RoPE(q_pe)] and the fp8_ds_mla insert of
-// [kv_c_normed | RoPE(k_pe)], in one launch.
+// MLA decode and prefill epilogues for gfx950, each one launch.
+//
+// Decode: the latent decode query mqa_q = [ql_nope | RoPE(q_pe)] and the
+// fp8_ds_mla insert of [kv_c_normed | RoPE(k_pe)].
+//
+// Prefill (fused_mla_key_concat_ds_mla_insert on the same page): RoPE on the
+// rope part of q in place, the bf16 full key k_out = [k_nope | RoPE(k_pe)]
+// for every head, and the same insert.
 //
 // What it computes is fused_mla_decode_q_concat_kv_cache_insert with
 // ds_mla=True (vLLM API page
@@ -92,7 +97,73 @@ __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogu
   }
 }
 
+__global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilogueArgs a) {
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const float *cs = nullptr;
+  if (a.positions) {
+    int64_t pos = a.positions[b];
+    pos = pos < 0 ? 0 : (pos >= a.max_position ? a.max_position - 1 : pos);
+    cs = a.cos_sin + pos * kRope;
+  }
+
+  // ---- the record (wave 0)
+  if (tid < 64) {
+    const int64_t slot = a.slots[b];
+    if (slot >= 0 && slot < a.num_records) {
+      const int lane = tid;
+      const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
+      uint32_t w = lane < 32 ? pe[lane] : 0u;
+      if (cs && lane < 32) w = rope_word(w, cs[lane], cs[32 + lane]);
+      write_record_wave(lane, a.kv_c + b * a.kv_c_stride, w, a.records + slot * kRecordBytes);
+    }
+  }
+
+  // ---- k_out = [k_nope | RoPE(k_pe)] and, with RoPE, q's rope part in
+  // place: per head, nope / 8 key chunks from k_nope, 8 rotated k_pe chunks
+  // (the same for every head) and 8 q chunks.
+  const int nk = a.nope / 8;
+  const int per_head = nk + 8 + (cs ? 8 : 0);
+  const int chunks = a.num_heads * per_head;
+  const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
+  for (int c = tid; c < chunks; c += kThreads) {
+    const int h = c / per_head;
+    const int j = c - h * per_head;
+    uint32_t w[4];
+    if (j < nk) {  // k_nope columns 8j .. 8j+7
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.k_nope + b * a.kn_stride_token +
+                                                               (int64_t)h * a.kn_stride_head + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = src[i];
+      uint32_t *dst = reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token + (int64_t)h * a.ko_stride_head + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = w[i];
+    } else if (j < nk + 8) {  // rope pairs 4jr .. 4jr+3 of k_pe
+      const int jr = j - nk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = cs ? rope_word(pe[4 * jr + i], cs[4 * jr + i], cs[32 + 4 * jr + i]) : pe[4 * jr + i];
+      uint32_t *dst = reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token + (int64_t)h * a.ko_stride_head +
+                                                   a.nope + 8 * jr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = w[i];
+    } else {  // q's rope pairs 4jr .. 4jr+3, in place
+      const int jr = j - nk - 8;
+      uint32_t *qp = reinterpret_cast<uint32_t *>(a.q + b * a.q_stride_token + (int64_t)h * a.q_stride_head +
+                                                  a.nope + 8 * jr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = rope_word(qp[i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qp[i] = w[i];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefill_epilogue(const PrefillEpilogueArgs &a, hipStream_t stream) {
+  prefill_epilogue_kernel<<<dim3((unsigned)a.num_tokens), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_epilogue(const DecodeEpilogueArgs &a, hipStream_t stream) {
   decode_epilogue_kernel<<<dim3((unsigned)a.num_tokens), dim3(kThreads), 0, stream>>>(a);

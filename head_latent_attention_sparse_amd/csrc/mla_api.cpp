@@ -509,4 +509,73 @@ mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int6
   return MLA_OK;
 }
 
+mla_status_t mla_prefill_key_concat_insert(void *q, int64_t q_stride_token, int64_t q_stride_head,
+                                           int32_t qk_nope_head_dim, const void *k_nope, int64_t k_nope_stride_token,
+                                           int64_t k_nope_stride_head, const void *kv_c, int64_t kv_c_stride_token,
+                                           const void *k_pe, int64_t k_pe_stride_token, const int64_t *slot_mapping,
+                                           int64_t num_tokens, int32_t num_heads, const int64_t *positions,
+                                           const float *cos_sin_cache, int64_t max_position, void *k_out,
+                                           int64_t k_out_stride_token, int64_t k_out_stride_head, void *kv_records,
+                                           int64_t num_records, int64_t record_stride, void *stream) {
+  const char *fn = "mla_prefill_key_concat_insert";
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_tokens %lld < 0", fn, (long long)num_tokens);
+  if (num_heads < 1 || num_heads > MLA_MAX_EPILOGUE_HEADS)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: num_heads %d outside 1..%d", fn, num_heads, MLA_MAX_EPILOGUE_HEADS);
+  if (qk_nope_head_dim < 8 || qk_nope_head_dim > 1024 || qk_nope_head_dim % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: qk_nope_head_dim %d (a multiple of 8 in 8..1024 is served)", fn,
+                qk_nope_head_dim);
+  const int64_t strides[8] = {q_stride_token,    q_stride_head,     k_nope_stride_token, k_nope_stride_head,
+                              kv_c_stride_token, k_pe_stride_token, k_out_stride_token,  k_out_stride_head};
+  for (int64_t st : strides) {
+    if (st < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative stride", fn);
+    if (st & 1) return fail(MLA_ERR_UNSUPPORTED, "%s: strides must be even (4-byte words)", fn);
+  }
+  if (!aligned(q, 4) || !aligned(k_nope, 4) || !aligned(kv_c, 4) || !aligned(k_pe, 4) || !aligned(k_out, 4))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: bf16 arrays must be 4-byte aligned", fn);
+  if (record_stride != MLA_RECORD_BYTES)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: record pitch %lld, only %d (unpadded) is served", fn, (long long)record_stride,
+                MLA_RECORD_BYTES);
+  if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_records %lld < 0", fn, (long long)num_records);
+  if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "%s: kv_records base not 16-byte aligned", fn);
+  if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: slot_mapping not 8-byte aligned", fn);
+  if ((positions == nullptr) != (cos_sin_cache == nullptr))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: positions and cos_sin_cache come together", fn);
+  if (positions) {
+    if (max_position < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: max_position %lld < 1", fn, (long long)max_position);
+    if (!aligned(positions, 8) || !aligned(cos_sin_cache, 4))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "%s: misaligned positions or cos_sin_cache", fn);
+  }
+  if (num_tokens == 0) return MLA_OK;
+  if (num_tokens > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
+  if (!k_nope || !kv_c || !k_pe || !slot_mapping || !k_out || (positions && !q))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL input or output", fn);
+  if (num_records > 0 && !kv_records) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL kv_records", fn);
+  mla::PrefillEpilogueArgs a;
+  a.q = static_cast<uint16_t *>(q);
+  a.q_stride_token = q_stride_token;
+  a.q_stride_head = q_stride_head;
+  a.nope = qk_nope_head_dim;
+  a.k_nope = static_cast<const uint16_t *>(k_nope);
+  a.kn_stride_token = k_nope_stride_token;
+  a.kn_stride_head = k_nope_stride_head;
+  a.kv_c = static_cast<const uint16_t *>(kv_c);
+  a.kv_c_stride = kv_c_stride_token;
+  a.k_pe = static_cast<const uint16_t *>(k_pe);
+  a.k_pe_stride = k_pe_stride_token;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.positions = positions;
+  a.cos_sin = cos_sin_cache;
+  a.max_position = max_position;
+  a.k_out = static_cast<uint16_t *>(k_out);
+  a.ko_stride_token = k_out_stride_token;
+  a.ko_stride_head = k_out_stride_head;
+  a.records = static_cast<uint8_t *>(kv_records);
+  a.num_records = num_records;
+  hipError_t e = mla::launch_prefill_epilogue(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return MLA_OK;
+}
+
 }  // extern "C"

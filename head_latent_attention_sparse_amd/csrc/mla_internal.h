@@ -78,6 +78,30 @@ struct DecodeEpilogueArgs {
 
 hipError_t launch_decode_epilogue(const DecodeEpilogueArgs &a, hipStream_t stream);
 
+struct PrefillEpilogueArgs {
+  uint16_t *q;  // [Tp, H, nope + 64]: RoPE in place on columns nope .. nope+63
+  int64_t q_stride_token, q_stride_head;
+  int32_t nope;  // qk_nope_head_dim, a multiple of 8
+  const uint16_t *k_nope;  // [Tp, H, nope]
+  int64_t kn_stride_token, kn_stride_head;
+  const uint16_t *kv_c;
+  int64_t kv_c_stride;
+  const uint16_t *k_pe;
+  int64_t k_pe_stride;
+  const int64_t *slots;
+  int64_t num_tokens;
+  int32_t num_heads;
+  const int64_t *positions;  // nullptr: no RoPE
+  const float *cos_sin;
+  int64_t max_position;
+  uint16_t *k_out;  // [Tp, H, nope + 64]
+  int64_t ko_stride_token, ko_stride_head;
+  uint8_t *records;
+  int64_t num_records;
+};
+
+hipError_t launch_prefill_epilogue(const PrefillEpilogueArgs &a, hipStream_t stream);
+
 struct GatherArgs {
   const uint8_t *records;
   int64_t num_records;

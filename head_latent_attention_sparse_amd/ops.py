@@ -49,6 +49,8 @@ SIGNATURES = {
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
     "mla_v_up_proj": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _I64, _I64, _P]),
     "mla_gather_upconvert": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _I32, _I64, _P, _I64, _P]),
+    "mla_prefill_key_concat_insert": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
+                                             _I32, _P, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "mla_decode_q_concat_insert": (_I32, [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P,
                                           _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
     "mla_last_error": (ctypes.c_char_p, []),
@@ -423,3 +425,71 @@ def v_up_proj(latent, w_uv, *, gate=None, out=None):
                              t_count, heads, out.data_ptr(), out.stride(0), out.stride(1), _stream(dev))
     _check(st)
     return out
+
+
+def key_concat_insert(q, k_nope, k_pe, kv_c_normed, kv_cache, slot_mapping, *, positions=None,
+                      cos_sin_cache=None, k_out=None):
+    """MLA prefill epilogue in one launch -> k_out [Tp, H, nope + 64] bf16.
+
+    k_out = [k_nope | k_pe] per head, [kv_c_normed | k_pe] inserted into the
+    fp8_ds_mla cache at slot_mapping (negative = skip); with ``positions`` /
+    ``cos_sin_cache`` GPT-J RoPE is applied to k_pe (in k_out and the
+    record) and to q[..., nope:] in place.  q [Tp, H, nope + 64] (may be
+    None without RoPE), k_nope [Tp, H, nope], k_pe [Tp, 64] or [Tp, 1, 64],
+    kv_c_normed [Tp, 512]; bf16 with a contiguous last dim.
+    """
+    if not (torch.is_tensor(k_nope) and k_nope.is_cuda and k_nope.ndim == 3):
+        raise ValueError("k_nope must be a CUDA bf16 tensor [Tp, H, nope]")
+    dev = k_nope.device
+    tp, heads, nope = k_nope.shape
+    if not 1 <= heads <= MAX_EPILOGUE_HEADS:
+        raise ValueError(f"{heads} heads: 1 .. {MAX_EPILOGUE_HEADS} are served")
+    _bf16_rows(k_nope, "k_nope", (heads, nope), dev)
+    if q is not None:
+        _bf16_rows(q, "q", (heads, nope + QK_ROPE_HEAD_DIM), dev)
+        if q.shape[0] != tp:
+            raise ValueError(f"q must have {tp} tokens")
+    elif positions is not None:
+        raise ValueError("q is needed with RoPE (it is rotated in place)")
+    _bf16_rows(kv_c_normed, "kv_c_normed", (KV_LORA_RANK,), dev)
+    if not (torch.is_tensor(k_pe) and k_pe.numel() == tp * QK_ROPE_HEAD_DIM):
+        raise ValueError("k_pe must hold 64 values per token")
+    k_pe2 = _bf16_rows(k_pe.reshape(tp, QK_ROPE_HEAD_DIM), "k_pe", (QK_ROPE_HEAD_DIM,), dev)
+    if kv_c_normed.shape[0] != tp:
+        raise ValueError(f"kv_c_normed must have {tp} tokens")
+    if not (torch.is_tensor(slot_mapping) and slot_mapping.dtype == torch.int64 and slot_mapping.ndim == 1
+            and slot_mapping.numel() == tp and slot_mapping.is_contiguous() and slot_mapping.device == dev):
+        raise ValueError("slot_mapping must be a contiguous int64 [Tp] tensor on k_nope's device")
+    if (positions is None) != (cos_sin_cache is None):
+        raise ValueError("positions and cos_sin_cache come together")
+    max_position = 0
+    if positions is not None:
+        if not (positions.dtype == torch.int64 and positions.ndim == 1 and positions.numel() == tp
+                and positions.is_contiguous() and positions.device == dev):
+            raise ValueError("positions must be a contiguous int64 [Tp] tensor on k_nope's device")
+        if not (cos_sin_cache.dtype == torch.float32 and cos_sin_cache.ndim == 2
+                and cos_sin_cache.shape[1] == QK_ROPE_HEAD_DIM and cos_sin_cache.is_contiguous()
+                and cos_sin_cache.device == dev):
+            raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, 64] tensor")
+        max_position = cos_sin_cache.shape[0]
+    if k_out is None:
+        k_out = torch.empty((tp, heads, nope + QK_ROPE_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _bf16_rows(k_out, "k_out", (heads, nope + QK_ROPE_HEAD_DIM), dev)
+    if not (torch.is_tensor(kv_cache) and kv_cache.device == dev):
+        raise ValueError("kv cache must be on k_nope's device")
+    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    L = lib()
+    with torch.cuda.device(dev):
+        st = L.mla_prefill_key_concat_insert(
+            q.data_ptr() if q is not None else None, q.stride(0) if q is not None else 0,
+            q.stride(1) if q is not None else 0, nope,
+            k_nope.data_ptr(), k_nope.stride(0), k_nope.stride(1),
+            kv_c_normed.data_ptr(), kv_c_normed.stride(0), k_pe2.data_ptr(), k_pe2.stride(0),
+            slot_mapping.data_ptr(), tp, heads,
+            positions.data_ptr() if positions is not None else None,
+            cos_sin_cache.data_ptr() if cos_sin_cache is not None else None, max_position,
+            k_out.data_ptr(), k_out.stride(0), k_out.stride(1),
+            kv_ptr, n_rec, pitch, _stream(dev))
+    _check(st)
+    return k_out

@@ -203,6 +203,37 @@ class DecodeEpilogueBatch:
     num_records: int
 
 
+@dataclass
+class PrefillEpilogueBatch:
+    """Inputs of one prefill epilogue call (RoPE on q, key concat, insert)."""
+    q: torch.Tensor               # bf16 [Tp, H, nope + 64]
+    k_nope: torch.Tensor          # bf16 [Tp, H, nope]
+    kv_c: torch.Tensor            # bf16 [Tp, 512]
+    k_pe: torch.Tensor            # bf16 [Tp, 64]
+    slots: torch.Tensor           # int64 [Tp], -1 = skip
+    positions: torch.Tensor       # int64 [Tp]
+    cos_sin_cache: torch.Tensor   # float32 [max_position, 64]
+    num_records: int
+
+
+def prefill_epilogue(tokens: int = 4096, heads: int = 16, nope: int = 128, pool: int = 131072,
+                     max_position: int = 65536, p_skip: float = 0.05, seed_offset: int = 10) -> PrefillEpilogueBatch:
+    """A prefill epilogue call: Tp tokens with H heads of q [nope | rope] and
+    k_nope, all N(0,1), their latent and rope N(0,1), at distinct random
+    slots (each -1 with probability p_skip), at consecutive positions from a
+    random start, with a standard rotary table."""
+    g = torch.Generator().manual_seed(SEED_BASE + seed_offset)
+    q = _bf16(g, (tokens, heads, nope + ROPE))
+    k_nope = _bf16(g, (tokens, heads, nope))
+    kv_c = _bf16(g, (tokens, LATENT))
+    k_pe = _bf16(g, (tokens, ROPE))
+    slots = torch.randperm(pool, generator=g)[:tokens].to(torch.int64)
+    slots[torch.rand(tokens, generator=g) < p_skip] = -1
+    start = int(torch.randint(0, max(max_position - tokens, 1), (1,), generator=g))
+    positions = torch.arange(start, start + tokens, dtype=torch.int64)
+    return PrefillEpilogueBatch(q, k_nope, kv_c, k_pe, slots, positions, rope_table(max_position), pool)
+
+
 def rope_table(max_position: int, dim: int = ROPE, base: float = 10000.0) -> torch.Tensor:
     """A rotary table as a model builds one: row p holds cos(p * f_i) for the
     dim/2 frequencies f_i = base^(-2i/dim), then sin(p * f_i); computed in

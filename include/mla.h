@@ -259,6 +259,41 @@ mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_t
                                         int64_t record_stride, void *stream);
 
 /*
+ * mla_prefill_key_concat_insert - the MLA prefill epilogue in one launch:
+ * GPT-J RoPE on the rope part of q in place, the bf16 full key
+ * k_out = [k_nope | RoPE(k_pe)] for every head, and the insert of
+ * [kv_c_normed | RoPE(k_pe)] into the fp8_ds_mla cache.
+ *
+ * Defined by fused_mla_key_concat_ds_mla_insert (fused_mla_key_concat_kv_cache
+ * page: "Concat full K (bf16) and insert the latent in the fp8_ds_mla
+ * layout"; q is [Tp, H, qk_head_dim] with RoPE applied in place, k_nope
+ * [Tp, H, qk_nope_head_dim], k_pe [Tp, 64], the returned key
+ * [Tp, H, qk_nope_head_dim + 64]).  RoPE, positions and cos_sin_cache as
+ * for mla_decode_q_concat_insert; without them q is left untouched and the
+ * key's rope part is k_pe bit for bit.  The record is written as by
+ * mla_cache_insert with the rotated k_pe.
+ *
+ *  q            bf16, element (t,h,d) at q + t*q_stride_token + h*q_stride_head
+ *               + d, d < qk_nope_head_dim + 64; only d >= qk_nope_head_dim is
+ *               written (and only with RoPE).  May be NULL without RoPE.
+ *  qk_nope_head_dim  a multiple of 8 in 8 .. 1024 (128 for the pages' model).
+ *  k_nope       bf16 [num_tokens, num_heads, qk_nope_head_dim] (strided).
+ *  kv_c, k_pe, slot_mapping, positions, cos_sin_cache, kv_records  as for
+ *               mla_decode_q_concat_insert.
+ *  k_out        bf16 output [num_tokens, num_heads, qk_nope_head_dim + 64].
+ * Strides in elements, even, >= 0; bf16 bases 4-byte aligned; outputs must
+ * not overlap inputs (q is updated in place only in its rope columns).
+ */
+mla_status_t mla_prefill_key_concat_insert(void *q, int64_t q_stride_token, int64_t q_stride_head,
+                                           int32_t qk_nope_head_dim, const void *k_nope, int64_t k_nope_stride_token,
+                                           int64_t k_nope_stride_head, const void *kv_c, int64_t kv_c_stride_token,
+                                           const void *k_pe, int64_t k_pe_stride_token, const int64_t *slot_mapping,
+                                           int64_t num_tokens, int32_t num_heads, const int64_t *positions,
+                                           const float *cos_sin_cache, int64_t max_position, void *k_out,
+                                           int64_t k_out_stride_token, int64_t k_out_stride_head, void *kv_records,
+                                           int64_t num_records, int64_t record_stride, void *stream);
+
+/*
  * mla_gather_upconvert - gather a context chunk's records through the block
  * table into a bf16 [num_tokens, 576] workspace (dequantized latent | rope).
  *
@@ -329,7 +364,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -33,7 +33,8 @@ Modules:
   e4m3       OCP float8 E4M3 ("fn") decode table and saturating RNE encoder.
   records    656-byte record encode (the insert writer) and decode.
   attention  Sparse attention forward over records, and the LSE merge.
-  epilogue   Decode epilogue: mqa_q concat, GPT-J RoPE, record insert.
+  epilogue   Decode and prefill epilogues: query / key concat, GPT-J RoPE,
+             record insert.
   gather     Context gather through the block table, upconverted to bf16.
   value      W_UV up-projection of the latent output, with the sigmoid gate.
 
@@ -48,6 +49,6 @@ from .records import (  # noqa: F401
     insert_records,
 )
 from .attention import merge_partials, sparse_fwd  # noqa: F401
-from .epilogue import decode_q_concat_insert, f32_to_bf16_bits, rope_gptj_bits  # noqa: F401
+from .epilogue import decode_q_concat_insert, f32_to_bf16_bits, key_concat_insert, rope_gptj_bits  # noqa: F401
 from .gather import gather_upconvert, upconvert_records  # noqa: F401
 from .value import v_up_proj  # noqa: F401

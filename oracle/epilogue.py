@@ -83,3 +83,34 @@ def decode_q_concat_insert(ql_nope_bits, q_pe_bits, kv_c_bits, k_pe_bits, slot_m
     if keep.any():
         pool[slots[keep]] = encode_records(np.asarray(kv_c_bits, dtype=np.uint16)[keep], kp[keep])
     return mqa, pool
+
+
+def key_concat_insert(q_bits, k_nope_bits, kv_c_bits, k_pe_bits, slot_mapping, pool,
+                      positions=None, cos_sin_cache=None):
+    """(q bits after RoPE, k_out bits uint16 [Tp, H, nope + 64], pool) for one
+    prefill step: ``fused_mla_key_concat_ds_mla_insert`` on the
+    fused_mla_key_concat_kv_cache page (full key [k_nope | k_pe] for every
+    head, q's rope part rotated in place, the latent inserted).
+
+    q_bits uint16 [Tp, H, nope + 64] (or None without RoPE); k_nope_bits
+    [Tp, H, nope]; kv_c_bits [Tp, 512]; k_pe_bits [Tp, 64]; the rest as for
+    decode_q_concat_insert.
+    """
+    kn = np.asarray(k_nope_bits, dtype=np.uint16)
+    kp = np.asarray(k_pe_bits, dtype=np.uint16).reshape(-1, ROPE)
+    tp, h, nope = kn.shape
+    q_out = None if q_bits is None else np.array(q_bits, dtype=np.uint16, copy=True)
+    if positions is not None:
+        table = np.asarray(cos_sin_cache, dtype=np.float32)
+        pos = np.clip(np.asarray(positions, dtype=np.int64), 0, table.shape[0] - 1)
+        rows = table[pos]
+        kp = rope_gptj_bits(kp, rows)
+        q_out[:, :, nope:] = rope_gptj_bits(q_out[:, :, nope:], rows[:, None, :])
+    k_out = np.empty((tp, h, nope + ROPE), dtype=np.uint16)
+    k_out[:, :, :nope] = kn
+    k_out[:, :, nope:] = kp[:, None, :]
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = (slots >= 0) & (slots < pool.shape[0])
+    if keep.any():
+        pool[slots[keep]] = encode_records(np.asarray(kv_c_bits, dtype=np.uint16)[keep], kp[keep])
+    return q_out, k_out, pool

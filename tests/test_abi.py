@@ -299,3 +299,37 @@ def test_fwd_ex_rejections(kw, status):
 def test_fwd_ex_zero_tokens_is_a_no_op():
     st, _ = fwd_ex(T=0, q=None, out=None, indptr=None, indices=None, lse=None)
     assert st == OK
+
+
+def prefill(**kw):
+    args = dict(q=A, qst=16 * 192, qsh=192, nope=128, kn=A, knt=16 * 128, knh=128, kv=A, kvt=512, kp=A, kpt=64,
+                slots=A, T=8, H=16, pos=None, cs=None, maxpos=0, ko=A, kot=16 * 192, koh=192, rec=A, n=100,
+                pitch=656, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_prefill_key_concat_insert(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nope=0), UNSUPPORTED),
+    (dict(nope=100), UNSUPPORTED),
+    (dict(nope=2048), UNSUPPORTED),
+    (dict(H=0), UNSUPPORTED),
+    (dict(knh=129), UNSUPPORTED),
+    (dict(qst=-2), INVALID),
+    (dict(ko=A + 2), UNSUPPORTED),
+    (dict(pos=A), INVALID),
+    (dict(pos=A, cs=A, maxpos=16, q=None), INVALID),
+    (dict(pitch=672), UNSUPPORTED),
+    (dict(kn=None), INVALID),
+])
+def test_prefill_rejections(kw, status):
+    st, msg = prefill(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_prefill_zero_tokens_is_a_no_op():
+    st, _ = prefill(T=0, q=None, kn=None, kv=None, kp=None, slots=None, ko=None)
+    assert st == OK

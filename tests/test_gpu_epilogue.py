@@ -1,7 +1,8 @@
-"""GPU parity of mla_decode_q_concat_insert (the decode epilogue) against the
-oracle: mqa_q and the pool bytes must be bit-exact (bf16 values and record
-bytes are integer patterns, and both sides round the same float32 RoPE
-arithmetic to bf16 to nearest even).
+"""GPU parity of the decode epilogue (mla_decode_q_concat_insert) and the
+prefill epilogue (mla_prefill_key_concat_insert) against the oracle: mqa_q,
+the rotated q, k_out and the pool bytes must be bit-exact (bf16 values and
+record bytes are integer patterns, and both sides round the same float32
+RoPE arithmetic to bf16 to nearest even).
 """
 
 import numpy as np
@@ -101,3 +102,45 @@ def test_epilogue_empty_and_rejections():
         mla.decode_q_concat_insert(*args, positions=z((2,), dtype=torch.int64, device=DEV),
                                    cos_sin_cache=z((4, 64), dtype=torch.float16, device=DEV))
     assert torch.all(pool == 0)
+
+
+# ---- prefill epilogue (mla_prefill_key_concat_insert)
+
+def run_prefill(w, rope, q_view=None, k_out=None):
+    from oracle import key_concat_insert as oracle_prefill
+    pool = torch.full((w.num_records, 656), FILL, dtype=torch.uint8, device=DEV)
+    q = (q_view if q_view is not None else w.q.to(DEV).clone())
+    ko = mla.key_concat_insert(q, w.k_nope.to(DEV), w.k_pe.to(DEV), w.kv_c.to(DEV), pool, w.slots.to(DEV),
+                               positions=w.positions.to(DEV) if rope else None,
+                               cos_sin_cache=w.cos_sin_cache.to(DEV) if rope else None, k_out=k_out)
+    torch.cuda.synchronize()
+    want_q, want_k, want_pool = oracle_prefill(
+        bf16_bits(w.q), bf16_bits(w.k_nope), bf16_bits(w.kv_c), bf16_bits(w.k_pe), w.slots.numpy(),
+        np.full((w.num_records, 656), FILL, dtype=np.uint8),
+        w.positions.numpy() if rope else None, w.cos_sin_cache.numpy() if rope else None)
+    return bf16_bits(q), bf16_bits(ko), pool.cpu().numpy(), want_q, want_k, want_pool
+
+
+@pytest.mark.parametrize("tp,h,nope", [(1, 1, 128), (7, 16, 128), (300, 16, 128), (33, 4, 64), (20, 128, 128)])
+@pytest.mark.parametrize("rope", [False, True])
+def test_prefill_epilogue_bit_exact(tp, h, nope, rope):
+    say(f"prefill epilogue Tp={tp} H={h} nope={nope} rope={rope}")
+    w = workloads.prefill_epilogue(tokens=tp, heads=h, nope=nope, pool=4 * tp + 16, max_position=4096)
+    got_q, got_k, got_pool, want_q, want_k, want_pool = run_prefill(w, rope)
+    check(got_q, got_pool, want_q, want_pool)
+    bad = np.argwhere(got_k != want_k)
+    assert bad.size == 0, f"{len(bad)} k_out values differ, first {bad[:3].tolist()}"
+
+
+def test_prefill_epilogue_strided_and_full():
+    say("prefill epilogue strided views, Tp=4096 full")
+    w = workloads.prefill_epilogue()
+    tp, h = w.q.shape[0], w.q.shape[1]
+    qbuf = torch.full((tp, h, 200), -9.0, dtype=torch.bfloat16, device=DEV)
+    qbuf[:, :, :192] = w.q.to(DEV)
+    kbuf = torch.full((tp, h, 200), -9.0, dtype=torch.bfloat16, device=DEV)
+    got_q, got_k, got_pool, want_q, want_k, want_pool = run_prefill(w, True, q_view=qbuf[:, :, :192],
+                                                                    k_out=kbuf[:, :, :192])
+    check(got_q, got_pool, want_q, want_pool)
+    assert np.array_equal(got_k, want_k), "k_out differs"
+    assert torch.all(qbuf[:, :, 192:].cpu() == -9.0) and torch.all(kbuf[:, :, 192:].cpu() == -9.0)

@@ -139,3 +139,34 @@ def test_epilogue_clamps_positions_into_the_table():
     same, _ = decode_q_concat_insert(ql, qp, kv, kp, slots, np.zeros((200, 656), np.uint8),
                                      np.array([0, 0, 99, 99]), table)
     np.testing.assert_array_equal(mqa, same)
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_prefill_key_concat_insert(rope):
+    from oracle import key_concat_insert
+    rng = np.random.default_rng(9)
+    tp, h, nope, n = 11, 3, 128, 50
+    q = bits_of(rng.standard_normal((tp, h, nope + 64)))
+    kn = bits_of(rng.standard_normal((tp, h, nope)))
+    kv = bits_of(rng.standard_normal((tp, 512)))
+    kp = bits_of(rng.standard_normal((tp, 64)))
+    slots = rng.permutation(n)[:tp].astype(np.int64)
+    slots[::4] = -1
+    table = rope_table(64).numpy() if rope else None
+    pos = rng.integers(0, 64, tp) if rope else None
+    pool0 = np.random.default_rng(10).integers(0, 256, (n, 656), dtype=np.uint8)
+    q_out, k_out, pool = key_concat_insert(q, kn, kv, kp, slots, pool0.copy(), pos, table)
+    np.testing.assert_array_equal(k_out[:, :, :nope], kn)                 # the nope part verbatim
+    kp_used = np.stack([rope_gptj_bits(kp[t], table[pos[t]]) for t in range(tp)]) if rope else kp
+    for hh in range(h):
+        np.testing.assert_array_equal(k_out[:, hh, nope:], kp_used)        # one rope key for every head
+    np.testing.assert_array_equal(q_out[:, :, :nope], q[:, :, :nope])      # q's nope part untouched
+    if rope:
+        for t in range(tp):
+            np.testing.assert_array_equal(q_out[t, :, nope:], rope_gptj_bits(q[t, :, nope:], table[pos[t]]))
+    else:
+        np.testing.assert_array_equal(q_out, q)
+    keep = slots >= 0
+    np.testing.assert_array_equal(pool[slots[keep]], encode_records(kv[keep], kp_used[keep]))
+    untouched = np.setdiff1d(np.arange(n), slots[keep])
+    np.testing.assert_array_equal(pool[untouched], pool0[untouched])
