@@ -100,13 +100,18 @@ typedef enum mla_status {
  *               base 4-byte aligned.
  *  lse          float32 [T, num_heads] contiguous; required with
  *               MLA_FLAG_RETURN_LSE, ignored otherwise.
- *  workspace    scratch for the split-KV plan and partials of at least
- *               mla_sparse_fwd_workspace_size(...) bytes, 256-byte aligned,
- *               or NULL: the library then uses a buffer it owns per device
- *               (allocated on first need, grown when too small; growing
- *               calls hipMalloc, so call mla_workspace_reserve before
- *               stream capture).  The buffer must not be used by another
- *               call that may run at the same time.
+ *  workspace    scratch for the split-KV partials and row prefix, of at
+ *               least mla_sparse_fwd_workspace_size(...) bytes, 256-byte
+ *               aligned; used only when the call splits.  A caller-provided
+ *               buffer must not be used by another call that may run at the
+ *               same time.  NULL: the library uses a buffer it owns per
+ *               device (allocated on first need, grown when too small;
+ *               growing frees the old buffer with hipFree, which waits for
+ *               the device, then calls hipMalloc, so call
+ *               mla_workspace_reserve before stream capture).  Every call
+ *               that passes NULL on a device shares that device's buffer:
+ *               two such calls that may overlap (different streams, or
+ *               several host threads) race, so give each its own workspace.
  *  stream       hipStream_t as void*.
  * Returns MLA_OK when the work is queued.
  */
