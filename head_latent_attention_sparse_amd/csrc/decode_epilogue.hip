@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunksPerHead = kQkDim / 8;  // 72 x 8 bf16
+constexpr int kBatch = 8;                   // chunks in flight per thread
 
 #pragma clang fp contract(off)
 // GPT-J rotation of one pair, float32 with a rounding after every operation.
@@ -69,31 +70,42 @@ __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogu
     }
   }
 
-  // ---- the query: chunk j of head h holds columns 8j .. 8j+7 of the 576
+  // ---- the query: chunk j of head h holds columns 8j .. 8j+7 of the 576.
+  // Batches of kBatch chunks per thread: all loads first, then the stores
+  // (the output may alias the inputs as far as the compiler knows, so loads
+  // after a store would wait for it).
   const int chunks = a.num_heads * kChunksPerHead;
-  for (int c = tid; c < chunks; c += kThreads) {
-    const int h = c / kChunksPerHead;
-    const int j = c - h * kChunksPerHead;
-    uint32_t w[4];
-    if (j < kLatent / 8) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.ql_nope + b * a.ql_stride_token +
-                                                               (int64_t)h * a.ql_stride_head + 8 * j);
+  for (int base = 0; base < chunks; base += kThreads * kBatch) {
+    u32x4_t w[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = src[i];
-    } else {
-      const int jr = j - kLatent / 8;  // rope pairs 4jr .. 4jr+3
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.q_pe + b * a.qpe_stride_token +
-                                                               (int64_t)h * a.qpe_stride_head + 8 * jr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = src[i];
-      if (cs) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = rope_word(w[i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
-      }
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = base + tid + kThreads * k;
+      if (c >= chunks) break;
+      const int h = c / kChunksPerHead;
+      const int j = c - h * kChunksPerHead;
+      const uint32_t *src = j < kLatent / 8
+                                ? reinterpret_cast<const uint32_t *>(a.ql_nope + b * a.ql_stride_token +
+                                                                     (int64_t)h * a.ql_stride_head + 8 * j)
+                                : reinterpret_cast<const uint32_t *>(a.q_pe + b * a.qpe_stride_token +
+                                                                     (int64_t)h * a.qpe_stride_head + 8 * (j - kLatent / 8));
+      w[k] = u32x4_t{src[0], src[1], src[2], src[3]};
     }
-    uint32_t *dst = reinterpret_cast<uint32_t *>(a.mqa_q + b * a.mq_stride_token + (int64_t)h * a.mq_stride_head + 8 * j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = w[i];
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = base + tid + kThreads * k;
+      if (c >= chunks) break;
+      const int h = c / kChunksPerHead;
+      const int j = c - h * kChunksPerHead;
+      if (cs && j >= kLatent / 8) {
+        const int jr = j - kLatent / 8;  // rope pairs 4jr .. 4jr+3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[k][i] = rope_word(w[k][i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
+      }
+      uint32_t *dst =
+          reinterpret_cast<uint32_t *>(a.mqa_q + b * a.mq_stride_token + (int64_t)h * a.mq_stride_head + 8 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = w[k][i];
+    }
   }
 }
 
@@ -126,34 +138,49 @@ __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilo
   const int per_head = nk + 8 + (cs ? 8 : 0);
   const int chunks = a.num_heads * per_head;
   const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
-  for (int c = tid; c < chunks; c += kThreads) {
-    const int h = c / per_head;
-    const int j = c - h * per_head;
-    uint32_t w[4];
-    if (j < nk) {  // k_nope columns 8j .. 8j+7
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.k_nope + b * a.kn_stride_token +
-                                                               (int64_t)h * a.kn_stride_head + 8 * j);
+  // kind of chunk j of a head: 0 = k_nope -> k_out, 1 = RoPE(k_pe) -> k_out,
+  // 2 = q's rope part in place.  Batches of kBatch chunks per thread: all
+  // loads first, then the stores (see the decode kernel).
+  for (int base = 0; base < chunks; base += kThreads * kBatch) {
+    u32x4_t w[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = src[i];
-      uint32_t *dst = reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token + (int64_t)h * a.ko_stride_head + 8 * j);
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = base + tid + kThreads * k;
+      if (c >= chunks) break;
+      const int h = c / per_head;
+      const int j = c - h * per_head;
+      const uint32_t *src;
+      if (j < nk)
+        src = reinterpret_cast<const uint32_t *>(a.k_nope + b * a.kn_stride_token + (int64_t)h * a.kn_stride_head + 8 * j);
+      else if (j < nk + 8)
+        src = pe + 4 * (j - nk);
+      else
+        src = reinterpret_cast<const uint32_t *>(a.q + b * a.q_stride_token + (int64_t)h * a.q_stride_head + a.nope +
+                                                 8 * (j - nk - 8));
+      w[k] = u32x4_t{src[0], src[1], src[2], src[3]};
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = w[i];
-    } else if (j < nk + 8) {  // rope pairs 4jr .. 4jr+3 of k_pe
-      const int jr = j - nk;
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = base + tid + kThreads * k;
+      if (c >= chunks) break;
+      const int h = c / per_head;
+      const int j = c - h * per_head;
+      uint32_t *dst;
+      if (j < nk) {
+        dst = reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token + (int64_t)h * a.ko_stride_head + 8 * j);
+      } else {
+        const int jr = j < nk + 8 ? j - nk : j - nk - 8;  // rope pairs 4jr .. 4jr+3
+        if (cs) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = cs ? rope_word(pe[4 * jr + i], cs[4 * jr + i], cs[32 + 4 * jr + i]) : pe[4 * jr + i];
-      uint32_t *dst = reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token + (int64_t)h * a.ko_stride_head +
-                                                   a.nope + 8 * jr);
+          for (int i = 0; i < 4; ++i) w[k][i] = rope_word(w[k][i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
+        }
+        dst = j < nk + 8 ? reinterpret_cast<uint32_t *>(a.k_out + b * a.ko_stride_token +
+                                                        (int64_t)h * a.ko_stride_head + a.nope + 8 * jr)
+                         : reinterpret_cast<uint32_t *>(a.q + b * a.q_stride_token + (int64_t)h * a.q_stride_head +
+                                                        a.nope + 8 * jr);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = w[i];
-    } else {  // q's rope pairs 4jr .. 4jr+3, in place
-      const int jr = j - nk - 8;
-      uint32_t *qp = reinterpret_cast<uint32_t *>(a.q + b * a.q_stride_token + (int64_t)h * a.q_stride_head +
-                                                  a.nope + 8 * jr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = rope_word(qp[i], cs[4 * jr + i], cs[32 + 4 * jr + i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qp[i] = w[i];
+      for (int i = 0; i < 4; ++i) dst[i] = w[k][i];
     }
   }
 }
