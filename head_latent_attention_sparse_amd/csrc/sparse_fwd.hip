@@ -656,24 +656,28 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
 // Combine a row's chunk partials: lse = log2 (sum_s 2^lse_s [+ 2^sink]),
 // out = sum_s 2^(lse_s - lse) o_s (an empty partial, lse_s = -inf, weighs 0;
 // the sink, when given, is one more term with a zero value; nothing at all
-// -> out 0, lse -inf).  One workgroup per (row,
-// head, 128-column quarter): 8 chunk lanes x 32 column quads accumulate and
-// reduce through LDS, so a row with many chunks is read by 256 threads.
+// -> out 0, lse -inf).  One workgroup per (row, head, 128-column quarter):
+// 8 chunk lanes x 32 column quads.  Each thread loads the LSEs and its
+// column quad of its chunks (s = lane, lane + 8, ...) at once, accumulates
+// them online (running max, rescaled sum and quad), and one LDS exchange
+// combines the 8 chunk lanes.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeChunkLanes = 8;
+constexpr int kMergeBatch = 8;  // chunks per thread with their loads in flight together
 
-__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
-  for (int m = 1; m < 64; m <<= 1) {
-    const float o = xor_shuffle(v, m);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();  // red may still be read by a previous reduction
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  v = red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) v = is_max ? fmaxf(v, red[w]) : v + red[w];
-  return v;
+struct MergeAcc {
+  float m, l;      // running max (log2 domain) and sum of 2^(lse - m)
+  floatx4_t o;     // running sum of 2^(lse - m) o
+};
+
+__device__ __forceinline__ void merge_add(MergeAcc &a, float lse, const floatx4_t &o) {
+  if (lse == -INFINITY) return;  // an empty partial weighs 0
+  const float m = fmaxf(a.m, lse);
+  const float sa = a.m == -INFINITY ? 0.f : fast_exp2(a.m - m);
+  const float w = fast_exp2(lse - m);
+  a.l = a.l * sa + w;
+  a.o = a.o * sa + o * w;
+  a.m = m;
 }
 
 template <bool kLse>
@@ -681,8 +685,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
                                                               const int32_t *prefix, int32_t heads, uint16_t *out,
                                                               int64_t o_st, int64_t o_sh, float *lse,
                                                               const float *sink) {
-  __shared__ floatx4_t s_part[kMergeChunkLanes][32];
-  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ MergeAcc s_acc[kMergeChunkLanes][32];
   const int tid = threadIdx.x;
   const int quarter = blockIdx.x & 3;
   const int64_t th = blockIdx.x >> 2;  // t * heads + h
@@ -691,39 +694,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
   const int64_t c0 = prefix[t];
   const int nc = prefix[t + 1] - (int)c0;
   const float *lp = ws_lse + c0 * heads + h;  // chunk s at lp[s * heads]
-
-  const float s2 = sink ? sink[h] * kLog2e : -INFINITY;
-  float mx = tid == 0 ? s2 : -INFINITY;
-  for (int s = tid; s < nc; s += kMergeThreads) mx = fmaxf(mx, lp[(int64_t)s * heads]);
-  mx = block_reduce(mx, s_red, true);
-  float tot = 0.f;
-  if (mx != -INFINITY) {
-    if (tid == 0) tot = fast_exp2(s2 - mx);
-    for (int s = tid; s < nc; s += kMergeThreads) tot += fast_exp2(lp[(int64_t)s * heads] - mx);
-  }
-  tot = block_reduce(tot, s_red, false);
-
   const int cl = tid >> 5;  // chunk lane
   const int cq = tid & 31;  // column quad
   const int col = quarter * 128 + 4 * cq;
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    for (int s = cl; s < nc; s += kMergeChunkLanes) {
-      const float w = fast_exp2(lp[(int64_t)s * heads] - mx);
-      const floatx4_t o = *reinterpret_cast<const floatx4_t *>(ws_out + ((c0 + s) * heads + h) * kLatent + col);
-      acc += o * w;
+  const float *op = ws_out + (c0 * heads + h) * kLatent + col;  // chunk s at op[s * heads * 512]
+
+  MergeAcc acc = {-INFINITY, 0.f, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  for (int base = cl; base < nc; base += kMergeChunkLanes * kMergeBatch) {
+    float ls[kMergeBatch];
+    floatx4_t os[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int s = base + kMergeChunkLanes * k;
+      const int sc = s < nc ? s : base;  // in range: base < nc
+      ls[k] = lp[(int64_t)sc * heads];
+      os[k] = *reinterpret_cast<const floatx4_t *>(op + (int64_t)sc * heads * kLatent);
+      if (s >= nc) ls[k] = -INFINITY;
     }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) merge_add(acc, ls[k], os[k]);
   }
-  s_part[cl][cq] = acc;
+  s_acc[cl][cq] = acc;
   __syncthreads();
   if (cl == 0) {
+    // the sink: one more term with a zero value
+    if (sink) merge_add(acc, sink[h] * kLog2e, floatx4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int k = 1; k < kMergeChunkLanes; ++k) acc += s_part[k][cq];
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    for (int k = 1; k < kMergeChunkLanes; ++k) {
+      const MergeAcc b = s_acc[k][cq];
+      if (b.m == -INFINITY) continue;
+      const float m = fmaxf(acc.m, b.m);
+      const float sa = acc.m == -INFINITY ? 0.f : fast_exp2(acc.m - m);
+      const float sb = fast_exp2(b.m - m);
+      acc.l = acc.l * sa + b.l * sb;
+      acc.o = acc.o * sa + b.o * sb;
+      acc.m = m;
+    }
+    const float inv = acc.l > 0.f ? 1.f / acc.l : 0.f;
     uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
-    dst[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    dst[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    if (kLse && quarter == 0 && cq == 0) lse[t * heads + h] = mx == -INFINITY ? -INFINITY : (mx + fast_log2(tot)) * kLn2;
+    dst[0] = pack_bf16x2(acc.o[0] * inv, acc.o[1] * inv);
+    dst[1] = pack_bf16x2(acc.o[2] * inv, acc.o[3] * inv);
+    if (kLse && quarter == 0 && cq == 0)
+      lse[t * heads + h] = acc.m == -INFINITY ? -INFINITY : (acc.m + fast_log2(acc.l)) * kLn2;
   }
 }
 
