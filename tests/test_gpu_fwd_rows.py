@@ -1,0 +1,77 @@
+"""The forward without split over many rows of mixed lengths, more rows
+than the chip holds workgroups at once: empty rows, rows of 1 and 2 key
+tiles, tile-aligned and ragged long rows, and a long row that is all
+masked, interleaved with a period coprime to any power-of-two grid.  Against
+the oracle on all rows (bar as for the forward)."""
+
+import numpy as np
+import pytest
+import torch
+
+import head_latent_attention_sparse_amd as mla
+from oracle import encode_records, sparse_fwd as oracle_fwd
+from head_latent_attention_sparse_amd.workloads import bf16_bits
+from tests.helpers import assert_fwd_close, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 192 ** -0.5
+# period 11: coprime to any power-of-two grid, so neighbouring workgroups see every kind
+PATTERN = [0, 1, 64, 65, 700, 128, 2, 200, 0, 191, 300]
+
+
+def make(seed, t, n, p_bad, heads=16):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((t, heads, 576), generator=g).to(torch.bfloat16)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
+    lens = np.array([PATTERN[i % len(PATTERN)] for i in range(t)], dtype=np.int64)
+    ptr = np.concatenate([[0], np.cumsum(lens)])
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g).numpy().astype(np.int64)
+    r = torch.rand(int(ptr[-1]), generator=g).numpy()
+    idx[r < p_bad] = -1
+    # one long row entirely masked
+    idx[ptr[4]:ptr[5]] = -1
+    return q, rec, ptr, idx
+
+
+def run(q, rec, ptr, idx, dtype, **kw):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out, lse = mla.sparse_fwd(t(bf16_bits(q)).view(torch.bfloat16), t(rec), t(ptr).to(dtype), t(idx).to(dtype),
+                              SCALE, has_invalid=True, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype", [torch.int32, torch.int64])
+def test_many_mixed_rows(dtype):
+    say(f"mixed rows T=1500 dtype={dtype}")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = max(1500, 2 * cus + 301)
+    q, rec, ptr, idx = make(21, t, 3000, 0.2)
+    assert mla.split_workgroups(t, idx.size, cus) == 0
+    out, lse = run(q, rec, ptr, idx, dtype)
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
+    assert_fwd_close(out, lse, ref_out, ref_lse, "mixed rows")
+
+
+def test_many_mixed_rows_with_sink_and_extra_segment():
+    say("mixed rows + sink + extra")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = max(1200, 2 * cus + 177)
+    q, rec, ptr, idx = make(22, t, 2000, 0.1, heads=12)
+    g = torch.Generator().manual_seed(23)
+    kv2 = torch.randn((900, 512), generator=g).to(torch.bfloat16)
+    pe2 = torch.randn((900, 64), generator=g).to(torch.bfloat16)
+    rec2 = encode_records(bf16_bits(kv2), bf16_bits(pe2))
+    lens2 = np.array([[0, 40, 3, 130][i % 4] for i in range(t)], dtype=np.int64)
+    ptr2 = np.concatenate([[0], np.cumsum(lens2)])
+    idx2 = torch.randint(-3, 905, (int(ptr2[-1]),), generator=g).numpy().astype(np.int64)
+    sink = (torch.randn((12,), generator=g) * 2).numpy().astype(np.float32)
+    tt = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out, lse = run(q, rec, ptr, idx, torch.int32, attn_sink=tt(sink), extra_kv=tt(rec2),
+                   extra_indptr=tt(ptr2).to(torch.int32), extra_indices=tt(idx2).to(torch.int32))
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE, extra=(rec2, ptr2, idx2), sink=sink)
+    assert_fwd_close(out, lse, ref_out, ref_lse, "mixed rows + sink + extra")
