@@ -16,9 +16,11 @@
 // (wave w owns output columns 32w .. 32w+31; the weight is brought in with
 // coalesced loads and transposed through LDS), and streams 32-row latent
 // tiles and their gate rows with a two-tile register pipeline (loads are
-// unconditional, so each wait covers exactly the tile it needs).  A tile's
-// 32 x 128 float32 result is staged in LDS, so the gate is applied and the
-// output written in coalesced 16-byte pieces.
+// unconditional, so each wait covers exactly the tile it needs).  With one
+// wave per SIMD nothing hides LDS latency, so each tile's A fragments are
+// read from LDS four k-steps ahead of their MFMAs.  A tile's 32 x 128
+// float32 result is staged in LDS, so the gate is applied and the output
+// written in coalesced 16-byte pieces.
 #include "device_utils.h"
 #include "mla_internal.h"
 
@@ -144,14 +146,31 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
     floatx4_t acc[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) acc[m][0] = acc[m][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // A fragments in blocks of kBlk k-steps, the next block's LDS reads
+    // issued before the current block's MFMAs (one wave per SIMD: nothing
+    // else would hide the LDS latency)
+    constexpr int kBlk = 4;
+    bf16x8_t af[2][2][kBlk];  // [buffer][m][k-step in block]
+    auto read_block = [&](int blk, bf16x8_t (&dst)[2][kBlk]) {
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u32x4_t *>(s_a + (16 * m + c) * kAPitch + 32 * s + 8 * g));
-        acc[m][0] = mfma_16x16x32_bf16(af, bw[s][0], acc[m][0]);
-        acc[m][1] = mfma_16x16x32_bf16(af, bw[s][1], acc[m][1]);
-      }
+        for (int i = 0; i < kBlk; ++i)
+          dst[m][i] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(s_a + (16 * m + c) * kAPitch + 32 * (kBlk * blk + i) + 8 * g));
+    };
+    read_block(0, af[0]);
+#pragma unroll
+    for (int blk = 0; blk < kKSteps / kBlk; ++blk) {
+      if (blk + 1 < kKSteps / kBlk) read_block(blk + 1, af[(blk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          acc[m][0] = mfma_16x16x32_bf16(af[blk & 1][m][i], bw[kBlk * blk + i][0], acc[m][0]);
+          acc[m][1] = mfma_16x16x32_bf16(af[blk & 1][m][i], bw[kBlk * blk + i][1], acc[m][1]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // D of m-tile m, n-tile j: lane (c, g) holds rows 16m + 4g + r, column 32 * wave + 16j + c
 #pragma unroll
@@ -199,12 +218,20 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
 
   // ---- two tiles in flight: while tile i is computed, tiles i+1 and i+2
   // are loading (into the register set tile i used, once it is in LDS).
-  for (; tile < tiles; tile += 2 * step) {
+  // The steady loop runs while both tiles it prefetches exist, so its loads
+  // are unconditional; the last (up to three) tiles follow with only the
+  // loads that exist.
+  for (; tile + 3 * step < tiles; tile += 2 * step) {
     compute_tile(tile, r0);
     load_tile(tile + 2 * step, r0);
-    if (tile + step >= tiles) break;
     compute_tile(tile + step, r1);
     load_tile(tile + 3 * step, r1);
+  }
+  if (tile < tiles) {
+    compute_tile(tile, r0);
+    if (tile + 2 * step < tiles) load_tile(tile + 2 * step, r0);
+    if (tile + step < tiles) compute_tile(tile + step, r1);
+    if (tile + 2 * step < tiles) compute_tile(tile + 2 * step, r0);
   }
 }
 
