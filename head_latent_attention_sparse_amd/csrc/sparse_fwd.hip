@@ -656,13 +656,14 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
 // Combine a row's chunk partials: lse = log2 (sum_s 2^lse_s [+ 2^sink]),
 // out = sum_s 2^(lse_s - lse) o_s (an empty partial, lse_s = -inf, weighs 0;
 // the sink, when given, is one more term with a zero value; nothing at all
-// -> out 0, lse -inf).  One workgroup per (row, head, 128-column quarter):
-// 8 chunk lanes x 32 column quads.  Each thread loads the LSEs and its
-// column quad of its chunks (s = lane, lane + 8, ...) at once, accumulates
-// them online (running max, rescaled sum and quad), and one LDS exchange
-// combines the 8 chunk lanes.
+// -> out 0, lse -inf).  A workgroup takes kLanes chunk lanes x (256 / kLanes)
+// column quads of one (row, head): 8 lanes cover a 128-column quarter of the
+// head, 4 lanes half of it, 2 lanes all of it, so rows cut into few chunks
+// use few, wide workgroups.  Each thread loads the LSEs and its column quad
+// of its chunks (s = lane, lane + kLanes, ...) at once, accumulates them
+// online (running max, rescaled sum and quad), and one LDS exchange combines
+// the chunk lanes.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunkLanes = 8;
 constexpr int kMergeBatch = 8;  // chunks per thread with their loads in flight together
 
 struct MergeAcc {
@@ -680,32 +681,34 @@ __device__ __forceinline__ void merge_add(MergeAcc &a, float lse, const floatx4_
   a.m = m;
 }
 
-template <bool kLse>
+template <bool kLse, int kLanes>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse,
                                                               const int32_t *prefix, int32_t heads, uint16_t *out,
                                                               int64_t o_st, int64_t o_sh, float *lse,
                                                               const float *sink) {
-  __shared__ MergeAcc s_acc[kMergeChunkLanes][32];
+  constexpr int kQuads = kMergeThreads / kLanes;
+  constexpr int kParts = kLatent / (4 * kQuads);
+  __shared__ MergeAcc s_acc[kLanes][kQuads];
   const int tid = threadIdx.x;
-  const int quarter = blockIdx.x & 3;
-  const int64_t th = blockIdx.x >> 2;  // t * heads + h
+  const int part = (int)(blockIdx.x % kParts);
+  const int64_t th = blockIdx.x / kParts;  // t * heads + h
   const int64_t t = th / heads;
   const int h = (int)(th - t * heads);
   const int64_t c0 = prefix[t];
   const int nc = prefix[t + 1] - (int)c0;
   const float *lp = ws_lse + c0 * heads + h;  // chunk s at lp[s * heads]
-  const int cl = tid >> 5;  // chunk lane
-  const int cq = tid & 31;  // column quad
-  const int col = quarter * 128 + 4 * cq;
+  const int cl = tid / kQuads;  // chunk lane
+  const int cq = tid % kQuads;  // column quad
+  const int col = part * 4 * kQuads + 4 * cq;
   const float *op = ws_out + (c0 * heads + h) * kLatent + col;  // chunk s at op[s * heads * 512]
 
   MergeAcc acc = {-INFINITY, 0.f, floatx4_t{0.f, 0.f, 0.f, 0.f}};
-  for (int base = cl; base < nc; base += kMergeChunkLanes * kMergeBatch) {
+  for (int base = cl; base < nc; base += kLanes * kMergeBatch) {
     float ls[kMergeBatch];
     floatx4_t os[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int s = base + kMergeChunkLanes * k;
+      const int s = base + kLanes * k;
       const int sc = s < nc ? s : base;  // in range: base < nc
       ls[k] = lp[(int64_t)sc * heads];
       os[k] = *reinterpret_cast<const floatx4_t *>(op + (int64_t)sc * heads * kLatent);
@@ -720,7 +723,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
     // the sink: one more term with a zero value
     if (sink) merge_add(acc, sink[h] * kLog2e, floatx4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int k = 1; k < kMergeChunkLanes; ++k) {
+    for (int k = 1; k < kLanes; ++k) {
       const MergeAcc b = s_acc[k][cq];
       if (b.m == -INFINITY) continue;
       const float m = fmaxf(acc.m, b.m);
@@ -734,9 +737,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
     uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
     dst[0] = pack_bf16x2(acc.o[0] * inv, acc.o[1] * inv);
     dst[1] = pack_bf16x2(acc.o[2] * inv, acc.o[3] * inv);
-    if (kLse && quarter == 0 && cq == 0)
+    if (kLse && part == 0 && cq == 0)
       lse[t * heads + h] = acc.m == -INFINITY ? -INFINITY : (acc.m + fast_log2(acc.l)) * kLn2;
   }
+}
+
+template <int kLanes>
+void launch_merge(const FwdArgs &a, hipStream_t stream) {
+  const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * (kLanes / 2)));
+  if (a.lse)
+    merge_kernel<true, kLanes><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
+                                                                    a.out_stride_token, a.out_stride_head, a.lse, a.sink);
+  else
+    merge_kernel<false, kLanes><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
+                                                                     a.out_stride_token, a.out_stride_head, nullptr, a.sink);
 }
 
 template <typename IdxT, bool kExtra>
@@ -782,13 +796,14 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   sparse_fwd_kernel<IdxT, true, false, kExtra><<<dim3((unsigned)a.chunk_bound), block, 0, stream>>>(k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * 4));
-  if (lse)
-    merge_kernel<true><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                           a.out_stride_token, a.out_stride_head, a.lse, a.sink);
+  // chunk lanes for the average chunks per row (one batch of loads each when they fit)
+  const int64_t per_row = (a.chunk_bound + a.num_tokens - 1) / a.num_tokens;
+  if (per_row <= 2 * kMergeBatch)
+    launch_merge<2>(a, stream);
+  else if (per_row <= 4 * kMergeBatch)
+    launch_merge<4>(a, stream);
   else
-    merge_kernel<false><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                            a.out_stride_token, a.out_stride_head, nullptr, a.sink);
+    launch_merge<8>(a, stream);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
-"""The forward without split over many rows of mixed lengths, more rows
-than the chip holds workgroups at once: empty rows, rows of 1 and 2 key
-tiles, tile-aligned and ragged long rows, and a long row that is all
-masked, interleaved with a period coprime to any power-of-two grid.  Against
-the oracle on all rows (bar as for the forward)."""
+"""The forward over many rows of mixed lengths, against the oracle on all
+rows (bar as for the forward).  Without split: more rows than the chip
+holds workgroups at once, with empty rows, rows of 1 and 2 key tiles,
+tile-aligned and ragged long rows, and a long row that is all masked,
+interleaved with a period coprime to any power-of-two grid.  With split:
+row counts that take each shape of the partial merge."""
 
 import numpy as np
 import pytest
@@ -75,3 +76,28 @@ def test_many_mixed_rows_with_sink_and_extra_segment():
                    extra_indptr=tt(ptr2).to(torch.int32), extra_indices=tt(idx2).to(torch.int32))
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE, extra=(rec2, ptr2, idx2), sink=sink)
     assert_fwd_close(out, lse, ref_out, ref_lse, "mixed rows + sink + extra")
+
+
+@pytest.mark.parametrize("t", [8, 20, 64, 300])
+def test_split_merge_shapes(t):
+    """Rows the library splits on its own, at row counts whose average chunk
+    count per row picks each merge shape (many chunks per row: 8 chunk lanes
+    per workgroup; fewer: 4; few: 2); one row empty, one all masked."""
+    say(f"split merge shape T={t}")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator().manual_seed(30 + t)
+    n = 4096
+    q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
+    lens = torch.randint(520, 1500 if t < 64 else 700, (t,), generator=g).numpy().astype(np.int64)
+    lens[t // 2] = 0
+    ptr = np.concatenate([[0], np.cumsum(lens)])
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g).numpy().astype(np.int64)
+    idx[torch.rand(int(ptr[-1]), generator=g).numpy() < 0.1] = -1
+    idx[ptr[1]:ptr[2]] = -1
+    assert mla.split_workgroups(t, idx.size, cus) > 0
+    out, lse = run(q, rec, ptr, idx, torch.int32)
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
+    assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t}")
