@@ -1,0 +1,158 @@
+"""The entry points under HIP graph capture (torch.cuda.graph): a decode
+step (epilogue with RoPE and insert -> split-KV forward -> W_UV
+up-projection with gate) and a prefill step (key epilogue with q RoPE in
+place and insert -> one-workgroup-per-row forward, int64 indices), each
+captured once and replayed several times.  Before each replay the program
+writes new inputs into the captured buffers and runs the same step eagerly
+from the same state; the replay must then reproduce the eager outputs and
+pool bytes bit for bit (the kernels are deterministic).  Unrelated eager
+work and synchronizations run between the replays.  No parity with the
+oracle is claimed here; the other GPU tests do that for each entry point."""
+
+import pytest
+import torch
+
+import head_latent_attention_sparse_amd as mla
+from head_latent_attention_sparse_amd import workloads
+from tests.helpers import say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SCALE = 192 ** -0.5
+REPLAYS = 3
+
+
+def bf16(g, shape, std=1.0):
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
+
+
+def csr(g, t, n, lo, hi, dtype):
+    lens = torch.randint(lo, hi, (t,), generator=g)
+    ptr = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lens, 0)])
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g)
+    idx[torch.rand(idx.numel(), generator=g) < 0.1] = -1
+    return ptr.to(dtype), idx.to(dtype)
+
+
+def fill_pool(g, n):
+    pool = torch.zeros((n, 656), dtype=torch.uint8, device=DEV)
+    mla.cache_insert(bf16(g, (n, 512)).to(DEV), bf16(g, (n, 64)).to(DEV),
+                     torch.arange(n, dtype=torch.int64).to(DEV), pool)
+    return pool
+
+
+def same(name, a, b):
+    assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                       b.view(torch.uint8) if b.dtype != torch.uint8 else b), f"{name}: replay differs from eager"
+
+
+def unrelated_eager_work():
+    x = torch.randn((1 << 20,), device=DEV)
+    torch.cuda.synchronize()
+    return float(x.abs().sum())
+
+
+def check_replays(step, inputs, fresh_inputs, outputs, pool):
+    """Capture `step`, then for each replay: new inputs, eager step from a
+    saved pool, restore the pool, replay, compare."""
+    for dst, src in zip(inputs, fresh_inputs(REPLAYS)):
+        dst.copy_(src)
+    step()  # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        for dst, src in zip(inputs, fresh_inputs(r)):
+            dst.copy_(src)
+        saved = [x.clone() for x in inputs]
+        before = pool.clone()
+        step()
+        torch.cuda.synchronize()
+        want = [x.clone() for x in outputs] + [pool.clone()]
+        pool.copy_(before)
+        for dst, src in zip(inputs, saved):  # steps may update inputs in place
+            dst.copy_(src)
+        unrelated_eager_work()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (got, exp) in enumerate(zip(list(outputs) + [pool], want)):
+            same(f"replay {r} output {i}", got, exp)
+        say(f"replay {r} matches")
+
+
+def test_decode_step_graph():
+    say("graph: decode step (epilogue -> split forward -> up-projection)")
+    g = torch.Generator().manual_seed(41)
+    b, h, n = 64, 16, 8192
+    pool = fill_pool(g, n)
+    table = workloads.rope_table(4096).to(DEV)
+    ptr, idx = csr(g, b, n, 600, 1500, torch.int32)
+    ql, qp = torch.empty((b, h, 512), dtype=torch.bfloat16, device=DEV), torch.empty((b, h, 64), dtype=torch.bfloat16, device=DEV)
+    kv, kp = torch.empty((b, 512), dtype=torch.bfloat16, device=DEV), torch.empty((b, 64), dtype=torch.bfloat16, device=DEV)
+    slots = torch.empty((b,), dtype=torch.int64, device=DEV)
+    pos = torch.empty((b,), dtype=torch.int64, device=DEV)
+    ip, ix = ptr.to(DEV), torch.empty_like(idx).to(DEV)
+    w_uv = bf16(g, (h, 512, 128), 512 ** -0.5).to(DEV)
+    gate = torch.empty((b, h * 128), dtype=torch.bfloat16, device=DEV)
+    mqa = torch.empty((b, h, 576), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((b, h, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((b, h), dtype=torch.float32, device=DEV)
+    vout = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
+    assert mla.split_workgroups(b, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count) > 0
+
+    def fresh(r):
+        gr = torch.Generator().manual_seed(100 + r)
+        sl = torch.randperm(n, generator=gr)[:b]
+        sl[::9] = -1
+        _, ixr = csr(gr, b, n, 600, 1500, torch.int32)
+        ixr = ixr[: ix.numel()] if ixr.numel() >= ix.numel() else torch.cat([ixr, ixr.new_full((ix.numel() - ixr.numel(),), -1)])
+        return [bf16(gr, (b, h, 512)), bf16(gr, (b, h, 64)), bf16(gr, (b, 512)), bf16(gr, (b, 64)), sl,
+                torch.randint(0, 4096, (b,), generator=gr), ixr, bf16(gr, (b, h * 128))]
+
+    def step():
+        mla.decode_q_concat_insert(ql, qp, kv, kp, pool, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
+        _, l = mla.sparse_fwd(mqa, pool, ip, ix, SCALE, has_invalid=True, out=out, return_lse=True)
+        lse.copy_(l)
+        mla.v_up_proj(out, w_uv, gate=gate, out=vout)
+
+    check_replays(step, [ql, qp, kv, kp, slots, pos, ix, gate], lambda r: [x.to(DEV) for x in fresh(r)],
+                  [mqa, out, lse, vout], pool)
+
+
+def test_prefill_step_graph():
+    say("graph: prefill step (key epilogue -> forward, int64 indices)")
+    g = torch.Generator().manual_seed(42)
+    t, h, n = 600, 16, 8192
+    pool = fill_pool(g, n)
+    table = workloads.rope_table(8192).to(DEV)
+    ptr, idx = csr(g, t, n, 64, 400, torch.int64)
+    q = torch.empty((t, h, 192), dtype=torch.bfloat16, device=DEV)
+    kn = torch.empty((t, h, 128), dtype=torch.bfloat16, device=DEV)
+    kv, kp = torch.empty((t, 512), dtype=torch.bfloat16, device=DEV), torch.empty((t, 64), dtype=torch.bfloat16, device=DEV)
+    slots = torch.empty((t,), dtype=torch.int64, device=DEV)
+    pos = torch.empty((t,), dtype=torch.int64, device=DEV)
+    ip, ix = ptr.to(DEV), torch.empty_like(idx).to(DEV)
+    mqa = torch.empty((t, h, 576), dtype=torch.bfloat16, device=DEV)
+    k_out = torch.empty((t, h, 192), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((t, h, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((t, h), dtype=torch.float32, device=DEV)
+    assert mla.split_workgroups(t, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count) == 0
+
+    def fresh(r):
+        gr = torch.Generator().manual_seed(200 + r)
+        sl = torch.randperm(n, generator=gr)[:t]
+        sl[::7] = -1
+        ixr = torch.randint(-1, n, (ix.numel(),), generator=gr)
+        return [bf16(gr, (t, h, 192)), bf16(gr, (t, h, 128)), bf16(gr, (t, 512)), bf16(gr, (t, 64)), sl,
+                torch.randint(0, 8192, (t,), generator=gr), ixr, bf16(gr, (t, h, 576))]
+
+    def step():
+        mla.key_concat_insert(q, kn, kp, kv, pool, slots, positions=pos, cos_sin_cache=table, k_out=k_out)
+        _, l = mla.sparse_fwd(mqa, pool, ip, ix, SCALE, has_invalid=True, out=out, return_lse=True)
+        lse.copy_(l)
+
+    check_replays(step, [q, kn, kv, kp, slots, pos, ix, mqa], lambda r: [x.to(DEV) for x in fresh(r)],
+                  [q, k_out, out, lse], pool)
