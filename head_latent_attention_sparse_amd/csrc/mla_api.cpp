@@ -215,6 +215,10 @@ mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_head
   a.lse = want_lse ? lse : nullptr;
   a.chunk_forced = forced_chunk;
   a.chunk_bound = bound;
+  // equal rows laid out back to back (a top-k selection) make nnz a multiple of T
+  a.row_len_guess = (bound == 0 && !has_extra && num_indices > 0 && num_indices % num_tokens == 0)
+                        ? num_indices / num_tokens
+                        : 0;
   a.ws_out = nullptr;
   a.ws_lse = nullptr;
   a.ws_prefix = nullptr;

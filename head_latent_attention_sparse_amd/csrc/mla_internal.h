@@ -27,6 +27,9 @@ struct FwdArgs {
   // (an upper bound on the number of chunks).  At most 512 rows.
   int32_t chunk_forced;
   int64_t chunk_bound;
+  // one workgroup per row: rows most likely start at t * row_len_guess
+  // (checked against indptr by each workgroup; 0 = no guess)
+  int64_t row_len_guess = 0;
   float *ws_out;       // [chunk_bound, H, 512] float32 partials
   float *ws_lse;       // [chunk_bound, H] float32 base-2 log-sum-exp
   int32_t *ws_prefix;  // [T + 1] first chunk of each row

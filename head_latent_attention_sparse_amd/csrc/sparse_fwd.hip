@@ -78,6 +78,7 @@ struct FwdKernelArgs {
   const void *eindices;
   int64_t ennz;
   const float *sink;  // [heads] sink logits (natural-log units of the scaled logits), or nullptr
+  int64_t guess_len;  // one workgroup per row: rows most likely start at t * guess_len (0: no guess)
 };
 
 // A workgroup's share of a row.  Entry v of the row (0 <= v < lenp + lene)
@@ -301,16 +302,59 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   const int n = lane & 15;  // MFMA row/column index of this lane
   const int g = lane >> 4;  // MFMA k-group of this lane
 
+  // Lane roles used before the row is known: MFMA (n, g) for the query,
+  // (record, 16-byte sub-chunk) for the gather (see below).
+  const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
+  const int gsub = tid & 3;
+  u32x4_t qr[2];    // query, rope part
+  uint32_t qx[16];  // query, 32 latent values
+  // Query loads are unconditional: a lane past the last head reads the last
+  // head's row and zeroes it.  rope part: bf16 MFMA A operand (row = head
+  // n); lane (n, g) k-slots j of step st <-> rope d = 16g + 8st + j (the
+  // record's rope bytes are read with the same mapping).  latent part: the
+  // 32 values of (head n, latent tile `wave`, k-block g).
+  auto load_query = [&](int64_t t) {
+    const int nq = n < p.heads ? n : p.heads - 1;
+    const uint32_t qkeep = n < p.heads ? 0xFFFFFFFFu : 0u;
+    const uint16_t *qrow = p.q + t * p.q_st + (int64_t)nq * p.q_sh;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + kLatent + 16 * g + 8 * st);
+      qr[st] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
+    }
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * wave + 32 * g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) qx[e] = src[e] & qkeep;
+  };
+
   // ---- this workgroup's entries: a whole row, or a chunk of one
   const IdxT *indices = static_cast<const IdxT *>(p.indices);
   const IdxT *eindices = static_cast<const IdxT *>(p.eindices);
   RowRange rr;
+  // A top-k selection gives every row the same length L, laid out back to
+  // back (nnz = T * L), so row t most likely starts at entry t * L.  The
+  // first entries are requested at that guess together with the query,
+  // while indptr is still on its way, and used if indptr agrees; so the
+  // first gather waits for one round trip less.
+  IdxT guess_id0 = 0, guess_t0 = 0, guess_t1 = 0;
+  int64_t guess_beg = -1;
   if (kSplit) {
     if (!split_plan<IdxT, kExtra>(p, s_rec, rr)) return;  // whole workgroup
+    load_query(rr.t);
   } else {
     const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
     rr.t = blockIdx.x;
-    clamp_range((int64_t)indptr[rr.t], (int64_t)indptr[rr.t + 1], p.nnz, rr.beg, rr.lenp);
+    const IdxT x0 = indptr[rr.t], x1 = indptr[rr.t + 1];
+    load_query(rr.t);
+    if (!kExtra && p.guess_len > 0) {
+      guess_beg = rr.t * p.guess_len;
+      auto at = [&](int64_t v) { return indices[guess_beg + v < p.nnz ? guess_beg + v : 0]; };
+      guess_id0 = at(grec);
+      guess_t0 = at(lane);
+      guess_t1 = at(kTileKeys + lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all of the above in flight before indptr is used
+    clamp_range((int64_t)x0, (int64_t)x1, p.nnz, rr.beg, rr.lenp);
     int64_t lene = 0;
     rr.ebeg = 0;
     if (kExtra) {
@@ -355,8 +399,6 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // because its logit is -inf and its softmax weight exactly 0.
   // Records r, r+4, r+8, r+12 share a 16-lane group: at a 164-dword pitch
   // they start 16 banks apart, so each 16-lane LDS store pass is conflict-free.
-  const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
-  const int gsub = tid & 3;
   u32x4_t pf[kChunksPerThread];
 #pragma unroll
   for (int i = 0; i < kChunksPerThread; ++i) pf[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -377,36 +419,23 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
   };
 
-  // ---- start the first tile early.  The query is requested first, then
+  // ---- start the first tile early.  The query was requested first, then
   // this thread's slot of tile 0 and the slots of tiles 0 and 1 (for the
-  // masks); tile 0's gather is issued as soon as its slot is in, and the
-  // query split is computed while the gather is in flight.  (The gather is
-  // conditional, so anything loaded after it would wait for it.)  Query loads
-  // are unconditional: a lane past the last head reads the last head's row
-  // and zeroes it.
-  const int nq = n < p.heads ? n : p.heads - 1;
-  const uint32_t qkeep = n < p.heads ? 0xFFFFFFFFu : 0u;
-  const uint16_t *qrow = p.q + t * p.q_st + (int64_t)nq * p.q_sh;
-  // rope part: bf16 MFMA A operand (row = head n); lane (n, g) k-slots j of
-  // step st <-> rope d = 16g + 8st + j; the record's rope bytes are read with
-  // the same mapping.
-  u32x4_t qr[2];
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + kLatent + 16 * g + 8 * st);
-    qr[st] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
+  // masks) are taken from the guess or requested now; tile 0's gather is
+  // issued as soon as its slot is in, and the query split is computed while
+  // the gather is in flight.  (The gather is conditional, so anything
+  // loaded after it would wait for it.)
+  const bool guessed = guess_beg == rr.beg && rr.vb == 0 && rr.ve == p.guess_len;
+  IdxT my_id0, slot_t0, slot_t1;
+  if (guessed) {
+    my_id0 = guess_id0;
+    slot_t0 = guess_t0;
+    slot_t1 = guess_t1;
+  } else {
+    my_id0 = fetch_entry(0, grec);
+    slot_t0 = fetch_entry(0, lane);
+    slot_t1 = fetch_entry(1, lane);
   }
-  // latent part: the 32 values of (head n, latent tile `wave`, k-block g)
-  uint32_t qx[16];
-  {
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * wave + 32 * g);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) qx[e] = src[e] & qkeep;
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the slot loads
-  const IdxT my_id0 = fetch_entry(0, grec);
-  const IdxT slot_t0 = fetch_entry(0, lane);
-  const IdxT slot_t1 = fetch_entry(1, lane);
 
   // ---- query, latent part: two E4M3 terms per 32-element group, so that
   // QK^T runs on the records' E4M3 codes directly (scaled fp8 MFMA, no code
@@ -425,7 +454,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   {
     uint8_t *q_lds = s_rec;                     // [(blk * 2 + part) * 16 + h][128] codes
     uint8_t *sc_lds = s_rec + 4 * 2 * 16 * 128;  // [(part * 16 + h) * 4 + kb] words, byte blk
-    issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0, in flight during the split
+    // The query is in by the time the slot of tile 0 is (it was requested
+    // first); it is unpacked before the gather is issued, so the split after
+    // it does not wait for the gather.
     float x[32];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -435,6 +466,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    asm volatile("" : : "v"(amax));  // computed here, not sunk past the gather
+    issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0, in flight during the split
     uint32_t hw[8], lw[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) hw[i] = lw[i] = 0u;
@@ -782,6 +815,7 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   k.eindices = a.extra_indices;
   k.ennz = a.extra_num_indices;
   k.sink = a.sink;
+  k.guess_len = a.row_len_guess;
   const dim3 block(kThreads);
   const bool lse = a.lse != nullptr;
   if (a.chunk_bound <= 0) {
