@@ -333,3 +333,46 @@ def test_prefill_rejections(kw, status):
 def test_prefill_zero_tokens_is_a_no_op():
     st, _ = prefill(T=0, q=None, kn=None, kv=None, kp=None, slots=None, ko=None)
     assert st == OK
+
+
+C_PROGRAM = r"""
+#include "mla.h"
+#include <stdio.h>
+#include <string.h>
+
+int main(void) {
+  mla_status_t st;
+  if (mla_abi_version() != MLA_ABI_VERSION) return 1;
+  if (mla_status_string(MLA_OK) == NULL || mla_status_string(MLA_ERR_INVALID_ARGUMENT) == NULL) return 2;
+  /* a rejected forward (17 heads): nothing is queued, the message says why */
+  st = mla_sparse_fwd(NULL, 4, 17, 17 * MLA_QK_DIM, MLA_QK_DIM, NULL, 0, MLA_RECORD_BYTES, NULL, NULL, 0,
+                      1.0f, MLA_FLAG_RETURN_LSE, NULL, 17 * MLA_KV_LORA_RANK, MLA_KV_LORA_RANK, NULL, NULL, 0, NULL);
+  if (st == MLA_OK || strlen(mla_last_error()) == 0) return 3;
+  /* the split-KV launch size from host values only */
+  if (mla_sparse_fwd_split_workgroups(8, 8 * 131072, 256, 0u) != 512) return 4;
+  if (mla_sparse_fwd_split_workgroups(4096, (int64_t)4096 * 2048, 256, 0u) != 0) return 5;
+  puts("ok");
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/mla.h is a C header: a C99 program (pedantic, warnings as
+    errors) includes it, links libmla.so and calls host-only entry points."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib = mla.lib()  # the built library (loads or raises)
+    libdir = os.path.dirname(ops.LIB_PATH)
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe), "-L", libdir, "-lmla", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+    assert lib is not None
