@@ -69,8 +69,17 @@ def log(msg):
 
 
 def source_hash():
-    with open(FWD_KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernel's source with comments and blank space
+    removed, so the stored counters stay valid across comment edits and
+    lapse with any change to the code."""
+    import re
+
+    with open(FWD_KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def main():

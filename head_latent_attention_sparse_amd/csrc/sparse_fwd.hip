@@ -32,7 +32,10 @@
 //    conversion, so each lane ends up owning one head;
 //  * when there are too few rows to fill the GPU, rows are cut into chunks
 //    planned on the device (split_plan), each chunk's float32 partial and
-//    base-2 LSE go to a workspace, and merge_kernel combines them.
+//    base-2 LSE go to a workspace, and merge_kernel combines them;
+//  * with one workgroup per row and rows of equal length laid out back to
+//    back (a top-k selection), each workgroup fetches its first slot ids at
+//    the guessed row start while its indptr pair is still in flight.
 #include "device_utils.h"
 #include "mla_internal.h"
 
