@@ -181,6 +181,17 @@ def main():
     pairs_h = nnz * heads
     value = pairs_h / (ms_per_step * 1e-3)
     gathered = nnz_valid * 656.0
+    # every byte the call must move once: records gathered, the query, the CSR
+    # lists, out and lse (plus the second list and the sinks when given)
+    total_bytes = (gathered + q.numel() * 2 + indptr.numel() * indptr.element_size()
+                   + indices.numel() * indices.element_size() + out.numel() * 2
+                   + (t_count * heads * 4 if w.return_lse else 0))
+    if ex:
+        total_bytes += (ex["extra_indptr"].numel() * ex["extra_indptr"].element_size()
+                        + ex["extra_indices"].numel() * ex["extra_indices"].element_size() + heads * 4)
+    # inserts inside the step: [kv_c | k_pe] and the slot read, a record written
+    for kv_c, k_pe, slots in step_inserts:
+        total_bytes += kv_c.numel() * 2 + k_pe.numel() * 2 + slots.numel() * 8 + int((slots >= 0).sum()) * 656
     flops = nnz_valid * heads * 2.0 * (576 + 512)
     achieved_gbps = gathered / (dev_ms * 1e-3) / 1e9
 
@@ -217,6 +228,8 @@ def main():
             "parallelism": "single GPU",
         },
         "gathered_record_GBps": gathered / (ms_per_step * 1e-3) / 1e9,
+        "total_algorithmic_bytes": total_bytes,
+        "total_algorithmic_GBps": total_bytes / (dev_ms * 1e-3) / 1e9,
         "valid_pairs_H_per_s": nnz_valid * heads / (ms_per_step * 1e-3),
         "device_ms_per_step": dev_ms,
         "mfma_tflops": flops / (dev_ms * 1e-3) / 1e12,
