@@ -103,17 +103,19 @@ def test_split_merge_shapes(t):
     assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t}")
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("layout", ["equal", "alternating", "two_shifted", "equal_int64"])
-def test_row_start_guess(layout):
-    """nnz a multiple of T makes each row workgroup guess that row t starts
-    at t * nnz / T and fetch its first entries there before indptr arrives.
-    Rows where indptr agrees (start and length) use the guess, the others
-    fetch again: all rows equal; lengths alternating L + 5, L - 5 (even rows
-    start at the guess but are longer, odd rows start elsewhere); two rows
-    shifted by 7 entries inside an otherwise equal layout.  Against the
-    oracle on all rows."""
-    say(f"row start guess: {layout}")
-    t, length, n = 600, 150, 3000
+def test_row_start_guess(layout, split):
+    """nnz a multiple of T makes each one-row workgroup guess that row t
+    starts at t * nnz / T and fetch its first entries there before indptr
+    arrives; workgroups whose guess indptr confirms use it, the others fetch
+    again.  Layouts: all rows equal; lengths alternating L + 5, L - 5 (even
+    rows start at the guess, odd rows elsewhere); two rows shifted by 7
+    entries inside an otherwise equal layout.  Without split: 600 rows of
+    150; the same layouts also go through the library's split pass (16 rows
+    of 2000), which takes no guess.  Against the oracle on all rows."""
+    say(f"row start guess: {layout} split={split}")
+    t, length, n = (16, 2000, 3000) if split else (600, 150, 3000)
     g = torch.Generator().manual_seed(50)
     q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
     kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
@@ -123,12 +125,13 @@ def test_row_start_guess(layout):
     if layout == "alternating":
         ptr[1:-1:2] += 5
     elif layout == "two_shifted":
-        ptr[11] += 7
-        ptr[300] -= 7
+        ptr[t // 50 + 1] += 7
+        ptr[t // 2] -= 7
     idx = torch.randint(0, n, (t * length,), generator=g).numpy().astype(np.int64)
     idx[torch.rand(t * length, generator=g).numpy() < 0.1] = -1
     dtype = torch.int64 if layout == "equal_int64" else torch.int32
-    assert mla.split_workgroups(t, idx.size, torch.cuda.get_device_properties(0).multi_processor_count) == 0
+    wgs = mla.split_workgroups(t, idx.size, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert (wgs > 0) == split
     out, lse = run(q, rec, ptr, idx, dtype)
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
-    assert_fwd_close(out, lse, ref_out, ref_lse, f"guess {layout}")
+    assert_fwd_close(out, lse, ref_out, ref_lse, f"guess {layout} split={split}")
