@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture (torch.cuda.graph): a decode
 step (epilogue with RoPE and insert -> split-KV forward -> W_UV
 up-projection with gate) and a prefill step (key epilogue with q RoPE in
-place and insert -> one-workgroup-per-row forward, int64 indices), each
+place and insert -> plain insert -> one-workgroup-per-row forward, int64
+indices -> context gather through a block table), each
 captured once and replayed several times.  Before each replay the program
 writes new inputs into the captured buffers and runs the same step eagerly
 from the same state; the replay must then reproduce the eager outputs and
@@ -123,11 +124,11 @@ def test_decode_step_graph():
 
 
 def test_prefill_step_graph():
-    say("graph: prefill step (key epilogue -> forward, int64 indices)")
+    say("graph: prefill step (key epilogue -> insert -> forward, int64 indices -> gather)")
     g = torch.Generator().manual_seed(42)
     t, h, n = 600, 16, 8192
     pool = fill_pool(g, n)
-    table = workloads.rope_table(8192).to(DEV)
+    rope = workloads.rope_table(8192).to(DEV)
     ptr, idx = csr(g, t, n, 64, 400, torch.int64)
     q = torch.empty((t, h, 192), dtype=torch.bfloat16, device=DEV)
     kn = torch.empty((t, h, 128), dtype=torch.bfloat16, device=DEV)
@@ -140,6 +141,14 @@ def test_prefill_step_graph():
     out = torch.empty((t, h, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((t, h), dtype=torch.float32, device=DEV)
     assert mla.split_workgroups(t, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count) == 0
+    # a plain insert of 256 more tokens, then a context gather of 4 requests
+    # of 300 tokens through a block table of 16-record blocks
+    kv2 = torch.empty((256, 512), dtype=torch.bfloat16, device=DEV)
+    kp2 = torch.empty((256, 64), dtype=torch.bfloat16, device=DEV)
+    slots2 = torch.empty((256,), dtype=torch.int64, device=DEV)
+    table = torch.randperm(n // 16, generator=g)[: 4 * 19].reshape(4, 19).to(torch.int32).to(DEV)
+    cu = torch.tensor([0, 300, 600, 900, 1200], dtype=torch.int32, device=DEV)
+    gdst = torch.empty((1200, 576), dtype=torch.bfloat16, device=DEV)
 
     def fresh(r):
         gr = torch.Generator().manual_seed(200 + r)
@@ -147,12 +156,15 @@ def test_prefill_step_graph():
         sl[::7] = -1
         ixr = torch.randint(-1, n, (ix.numel(),), generator=gr)
         return [bf16(gr, (t, h, 192)), bf16(gr, (t, h, 128)), bf16(gr, (t, 512)), bf16(gr, (t, 64)), sl,
-                torch.randint(0, 8192, (t,), generator=gr), ixr, bf16(gr, (t, h, 576))]
+                torch.randint(0, 8192, (t,), generator=gr), ixr, bf16(gr, (t, h, 576)),
+                bf16(gr, (256, 512)), bf16(gr, (256, 64)), torch.randperm(n, generator=gr)[:256]]
 
     def step():
-        mla.key_concat_insert(q, kn, kp, kv, pool, slots, positions=pos, cos_sin_cache=table, k_out=k_out)
+        mla.key_concat_insert(q, kn, kp, kv, pool, slots, positions=pos, cos_sin_cache=rope, k_out=k_out)
+        mla.cache_insert(kv2, kp2, slots2, pool)
         _, l = mla.sparse_fwd(mqa, pool, ip, ix, SCALE, has_invalid=True, out=out, return_lse=True)
         lse.copy_(l)
+        mla.gather_upconvert(pool, table, cu, 1200, block_size=16, dst=gdst)
 
-    check_replays(step, [q, kn, kv, kp, slots, pos, ix, mqa], lambda r: [x.to(DEV) for x in fresh(r)],
-                  [q, k_out, out, lse], pool)
+    check_replays(step, [q, kn, kv, kp, slots, pos, ix, mqa, kv2, kp2, slots2],
+                  lambda r: [x.to(DEV) for x in fresh(r)], [q, k_out, out, lse, gdst], pool)
