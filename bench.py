@@ -2,7 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                 [--no-cpu-baseline] [--copy-calibration]
-                [--epilogue | --prefill-epilogue | --gather | --vproj | --with-sink-extra]
+                [--epilogue | --prefill-epilogue | --gather | --vproj | --decode-step | --with-sink-extra]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
@@ -12,8 +12,11 @@ decode epilogue call (mla_decode_q_concat_insert: 4096 tokens, 16 heads,
 RoPE), and with --gather one context-chunk gather + upconvert
 (mla_gather_upconvert: 64 requests of 1024..8192 tokens), and with --vproj
 one W_UV up-projection with the sigmoid gate (mla_v_up_proj: 4096 rows x 16
-heads).  Inputs are synthetic, seeded, and resident in HBM before timing
-starts.  Prints ONE JSON line.
+heads).  With --decode-step a step is one decode step of 64 requests over
+the paged decode workload (decode epilogue, split-KV forward, gated
+up-projection), timed eagerly and as a replayed HIP graph.  Inputs are
+synthetic, seeded, and resident in HBM before timing starts.  Prints ONE
+JSON line.
 """
 
 import argparse
@@ -59,6 +62,9 @@ def parse():
     ap.add_argument("--with-sink-extra", action="store_true",
                     help="forward variant: add per-head sink logits and a second segment of 256 entries per row "
                          "over a second 16384-record pool (mla_sparse_fwd_ex)")
+    ap.add_argument("--decode-step", action="store_true",
+                    help="measure one decode step on the paged decode workload (decode epilogue with RoPE and "
+                         "insert, split-KV forward, gated up-projection), eager and as a replayed HIP graph")
     ap.add_argument("--vproj", action="store_true",
                     help="measure the W_UV up-projection with the sigmoid gate instead of the forward")
     return ap.parse_args()
@@ -109,6 +115,9 @@ def main():
         return
     if args.vproj:
         bench_vproj(args, dev)
+        return
+    if args.decode_step:
+        bench_decode_step(args, dev)
         return
     log(f"generating workload {args.config}")
     w = workloads.CONFIGS[args.config]()
@@ -528,6 +537,99 @@ def bench_vproj(args, dev):
         result["cpu_baseline"] = {"value": t / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the whole call ({t} rows x {h} heads), numpy float64 oracle, "
                                             f"one thread, {el:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode_step(args, dev):
+    """One decode step of 64 requests, H = 16, over the paged decode
+    workload's pool and CSR lists: mla_decode_q_concat_insert (mqa_q with
+    RoPE, the new tokens' records), mla_sparse_fwd (split-KV pass and merge)
+    and mla_v_up_proj with the gate.  Timed eagerly and as one captured HIP
+    graph replayed per step, and as one graph of ten steps; `value` takes
+    the fastest of the three."""
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+    from head_latent_attention_sparse_amd import workloads
+
+    log("generating the decode step inputs")
+    w = workloads.paged_decode()
+    b, h = w.num_tokens, w.num_heads
+    pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=dev)
+    view = pool.view(-1, w.block_size, 656)
+    for ins in w.setup_inserts:
+        mla.cache_insert(ins.kv_c.to(dev), ins.k_pe.to(dev), ins.slots.to(dev), view)
+    e = workloads.decode_epilogue(batch=b, heads=h, pool=w.num_records, max_position=8192)
+    ql, qp, kv, kp = e.ql_nope.to(dev), e.q_pe.to(dev), e.kv_c.to(dev), e.k_pe.to(dev)
+    slots, pos, table = e.slots.to(dev), e.positions.to(dev), e.cos_sin_cache.to(dev)
+    vp = workloads.v_up_proj_inputs(tokens=b, heads=h)
+    w_uv, gate = vp.w_uv.to(dev), vp.gate.to(dev)
+    indptr, indices = w.indptr.to(dev), w.indices.to(dev)
+    mqa = torch.empty((b, h, 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((b, h, 512), dtype=torch.bfloat16, device=dev)
+    vout = torch.empty((b, h, 128), dtype=torch.bfloat16, device=dev)
+    ws_bytes = mla.lib().mla_sparse_fwd_workspace_size(b, h, w.nnz, 0, 0)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mla.decode_q_concat_insert(ql, qp, kv, kp, view, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
+        mla.sparse_fwd(mqa, view, indptr, indices, w.softmax_scale, out=out, return_lse=True, workspace=workspace)
+        mla.v_up_proj(out, w_uv, gate=gate, out=vout)
+
+    stream = torch.cuda.current_stream(dev)
+    eager_ms, eager_dev = time_steps(step, args, stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms, graph_dev = time_steps(graph.replay, args, torch.cuda.current_stream(dev))
+    # ten steps in one graph: per-replay costs spread over ten steps
+    graph10 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph10):
+        for _ in range(10):
+            step()
+    torch.cuda.synchronize()
+    g10_ms, g10_dev = time_steps(graph10.replay, args, torch.cuda.current_stream(dev))
+    g10_ms, g10_dev = g10_ms / 10, g10_dev / 10
+    assert torch.isfinite(vout.float()).all(), "non-finite output"
+
+    written = int((e.slots >= 0).sum())
+    moved = (w.nnz_valid() * 656.0                      # records gathered
+             + b * h * (512 + 64) * 2 + b * (512 + 64) * 2 + written * 656  # epilogue reads, records written
+             + b * h * 576 * 2 * 2                      # mqa_q written, then read by the forward
+             + b * h * 512 * 2 * 2                      # out written, then read by the up-projection
+             + w_uv.numel() * 2 + gate.numel() * 2 + vout.numel() * 2)
+    best_ms, best_dev = min((eager_ms, eager_dev), (graph_ms, graph_dev), (g10_ms, g10_dev), key=lambda x: x[1])
+    achieved = moved / (best_dev * 1e-3) / 1e9
+    result = {
+        "metric": "MLA decode step (epilogue + split-KV sparse forward + W_UV up-projection): steps/s",
+        "value": 1e3 / best_ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": best_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode step: B={b} requests, H={h}, contexts U[1024, 8192] over a paged pool "
+                               f"of {w.num_records} records, RoPE, gated up-projection",
+                   "parallelism": "single GPU"},
+        "device_ms_per_step": best_dev,
+        "eager_ms_per_step": eager_ms,
+        "eager_device_ms_per_step": eager_dev,
+        "graph_ms_per_step": graph_ms,
+        "graph_device_ms_per_step": graph_dev,
+        "graph10_ms_per_step": g10_ms,
+        "graph10_device_ms_per_step": g10_dev,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
+    }
+    log(f"device us/step: eager {eager_dev * 1e3:.1f}, graph of one step {graph_dev * 1e3:.1f}, "
+        f"graph of ten steps {g10_dev * 1e3:.1f}")
     print(json.dumps(result), flush=True)
 
 
