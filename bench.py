@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="workload: 1 tiny, 2 paged decode, 3 sparse top-k prefill, 4 long context, "
+                         "5 insert + attend")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -93,7 +95,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
-              "(rows would shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(rows would shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -120,7 +122,7 @@ def main():
         bench_decode_step(args, dev)
         return
     log(f"generating workload {args.config}")
-    w = workloads.CONFIGS[args.config]()
+    w = workloads.WORKLOADS[args.config]()
     t_count, heads = w.num_tokens, w.num_heads
     nnz, nnz_valid = w.nnz, w.nnz_valid()
 

@@ -341,7 +341,7 @@ def extra_segment(tokens: int, heads: int, per_row: int = 256, records: int = 16
     return ExtraSegment(fill, records, indptr, indices, sink)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: tiny,
     2: paged_decode,
     3: sparse_prefill,

@@ -10,7 +10,7 @@ head); ``lse`` is the natural-log log-sum-exp of ``softmax_scale * q.k``
 over the unmasked keys; a row with no unmasked key gives out = 0 and
 lse = -inf.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
 * slot ids >= the number of records are masked like negative ones (the
   pages leave them undefined; the HIP kernel masks them too, so no caller
   error can make it read outside the pool);

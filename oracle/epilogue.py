@@ -13,7 +13,7 @@ page ``MultiHeadLatentAttention`` builds its rotary table in float32 with
 ``is_neox_style=False`` and hands it to the fused epilogues, which read it in
 float32 and do the RoPE arithmetic in float32.
 
-Readings taken where the pages leave it open (listed in the design doc): the
+Readings taken where the pages leave it open: the
 table row of a position holds the 32 cosines then the 32 sines of the 32
 rotation pairs; GPT-J style pairs adjacent values (2i, 2i+1); each product
 and each sum is one float32 rounding (no fused multiply-add), and the

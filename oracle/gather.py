@@ -7,7 +7,7 @@ Follows ``cp_gather_and_upconvert_fp8_kv_cache`` as the
 (``dst = workspace[:toks]``, ``workspace_starts = chunk.cu_seq_lens``,
 ``seq_starts = chunk.starts``, a block table per request).
 
-Readings taken where the page gives only the call (listed in the design doc):
+Readings taken where the page gives only the call:
 workspace row ``cu[r] + j`` holds context position ``starts[r] + j`` of
 request r for ``j < cu[r+1] - cu[r]``; position p lives in record
 ``block_table[r][p // block_size] * block_size + p % block_size``; the row is

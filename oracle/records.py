@@ -10,9 +10,9 @@ docstrings; fused_mla_key_concat_kv_cache page,
     bytes 512 .. 527   four float32 scales, tile b covers latent [128b, 128b+128)
     bytes 528 .. 655   64 bf16 rope values
 
-Readings taken where the pages leave the writer open (each is listed in
-the design doc): little-endian scales and rope; the per-tile scale is the
-tile's absolute maximum divided by 448, in float32; codes are
+Readings taken where the pages leave the writer open: little-endian
+scales and rope; the per-tile scale is the tile's absolute maximum
+divided by 448, in float32; codes are
 E4M3(x / scale) with a correctly rounded float32 division and the
 saturating RNE encoder; an all-zero tile gets scale 0 and codes 0;
 records at negative slots are not written.  A slot addresses record

@@ -6,8 +6,7 @@ Follows ``_v_up_proj`` on the ``vllm.models.kimi_k3.nvidia.mla`` page: the
 [T, H, 512] latent output, viewed per head, times ``W_UV`` (the (N, L, V) =
 [H, 512, 128] weight ``process_weights_after_loading`` splits out of
 ``kv_b_proj``), then the layer's ``_gate_sigmoid_mul(attn_out, gate)`` with
-the g_proj output ``gate`` [T, H * 128].  Reading taken (listed in
-the design doc): the gate multiplies by the logistic sigmoid elementwise, column
+the g_proj output ``gate`` [T, H * 128].  Reading taken: the gate multiplies by the logistic sigmoid elementwise, column
 ``128 h + v`` of the gate belonging to head h, value v.  Computed in float64
 on the bf16 inputs (a per-head matrix product serves as the step).
 """
