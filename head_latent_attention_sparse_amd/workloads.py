@@ -94,7 +94,7 @@ def _pool_fill(g: torch.Generator, n: int, latent_std: float = 1.0) -> InsertBat
 
 
 def tiny(tokens: int = 4, heads: int = 16, records: int = 2048, per_row: int = 128) -> Workload:
-    """Config 1: 4 rows x 128 distinct random slots over a 2048-record cache."""
+    """Tiny: 4 rows x 128 distinct random slots over a 2048-record cache."""
     g = torch.Generator().manual_seed(SEED_BASE + 1)
     fill = _pool_fill(g, records)
     q = _bf16(g, (tokens, heads, D_QK))
@@ -106,7 +106,7 @@ def tiny(tokens: int = 4, heads: int = 16, records: int = 2048, per_row: int = 1
 
 def paged_decode(batch: int = 64, heads: int = 16, len_lo: int = 1024, len_hi: int = 8192,
                  block_size: int = 64) -> Workload:
-    """Config 2: one query row per request over a paged pool and a random block table.
+    """Paged decode: one query row per request over a paged pool and a random block table.
 
     Context lengths are uniform on [len_lo, len_hi] (inclusive).  The pool holds
     exactly the blocks the requests need; a random permutation of the blocks is
@@ -135,7 +135,7 @@ def paged_decode(batch: int = 64, heads: int = 16, len_lo: int = 1024, len_hi: i
 def sparse_prefill(tokens: int = 4096, heads: int = 16, records: int = 131072,
                    per_row: int = 2048, p_invalid: float = 0.10,
                    frac_empty: float = 0.01) -> Workload:
-    """Config 3: top-k style sparse prefill.
+    """Sparse top-k prefill.
 
     Each row lists ``per_row`` distinct uniform slots; then round(frac_empty * T)
     random rows are set entirely to -1, and every other entry is set to -1
@@ -157,7 +157,7 @@ def sparse_prefill(tokens: int = 4096, heads: int = 16, records: int = 131072,
 
 def long_context(tokens: int = 8, heads: int = 16, records: int = 131072,
                  latent_std: float = 2.0) -> Workload:
-    """Config 4: few rows, each a random permutation of the whole cache."""
+    """Long context: few rows, each a random permutation of the whole cache."""
     g = torch.Generator().manual_seed(SEED_BASE + 4)
     fill = _pool_fill(g, records, latent_std)
     q = _bf16(g, (tokens, heads, D_QK))
@@ -169,7 +169,7 @@ def long_context(tokens: int = 8, heads: int = 16, records: int = 131072,
 
 def insert_attend(pool: int = 65536, new_tokens: int = 4096, p_skip: float = 0.05,
                   tokens: int = 1024, heads: int = 12, per_row: int = 1024) -> Workload:
-    """Config 5: insert new tokens into a filled pool, then attend over it.
+    """Insert + attend: insert new tokens into a filled pool, then attend over it.
 
     The pool is first filled at every slot; the step inserts ``new_tokens``
     tokens at distinct random slots, each slot set to -1 (skipped) with

@@ -84,8 +84,8 @@ def decode_records(records):
     """Records uint8 [n, 656] -> (K float64 [n, 576], V float64 [n, 512]).
 
     latent[d] = E4M3(code[d]) * scale[d // 128], exact in float64; the key is
-    [latent | rope] and the value is the latent alone (benchmark spec
-    of the method; the output is 512 wide on the flydsl_sparse_mla page).
+    [latent | rope] and the value is the latent alone (the output is 512
+    wide on the flydsl_sparse_mla page).
     """
     records = np.asarray(records, dtype=np.uint8).reshape(-1, RECORD_BYTES)
     n = records.shape[0]

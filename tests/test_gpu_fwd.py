@@ -1,6 +1,6 @@
 """GPU parity of mla_sparse_fwd against the fp64 oracle.
 
-Bar (spec tolerance): |out - ref| <= 1e-2 + 1e-2 |ref| elementwise,
+Bar (the tolerance of the hot-path statement): |out - ref| <= 1e-2 + 1e-2 |ref| elementwise,
 |lse - ref| <= 2e-3, -inf exactly where the oracle has an empty row.  The
 GPU pools are built by mla_cache_insert and first checked byte for byte
 against the oracle's writer; the oracle works from its own records.
@@ -71,44 +71,44 @@ def check_all_rows_sane(w, out, lse):
     assert (out[empty] == 0).all()
 
 
-# ----------------------------------------------------------------- configs
+# --------------------------------------------------------------- workloads
 
-def test_config1_tiny_all_rows():
-    say("fwd config1 tiny")
+def test_tiny_all_rows():
+    say("fwd tiny")
     w = workloads.tiny()
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
-    check_rows(w, pool, out, lse, range(w.num_tokens), "config1")
+    check_rows(w, pool, out, lse, range(w.num_tokens), "tiny")
 
 
-def test_config2_paged_decode_reduced():
-    say("fwd config2 reduced (8 requests)")
+def test_paged_decode_reduced():
+    say("fwd paged decode reduced (8 requests)")
     w = workloads.paged_decode(batch=8)
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
-    check_rows(w, pool, out, lse, range(8), "config2-reduced")
+    check_rows(w, pool, out, lse, range(8), "paged decode-reduced")
 
 
-def test_config2_paged_decode_full_sampled():
-    say("fwd config2 full, 6 sampled rows")
+def test_paged_decode_full_sampled():
+    say("fwd paged decode full, 6 sampled rows")
     w = workloads.paged_decode()
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
     check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, [0, 9, 21, 37, 50, 63], "config2-full")
+    check_rows(w, pool, out, lse, [0, 9, 21, 37, 50, 63], "paged decode-full")
 
 
-def test_config3_sparse_prefill_reduced():
-    say("fwd config3 reduced (T=96, N=16384)")
+def test_sparse_prefill_reduced():
+    say("fwd sparse prefill reduced (T=96, N=16384)")
     w = workloads.sparse_prefill(tokens=96, records=16384, frac_empty=0.03)
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
     check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, range(96), "config3-reduced")
+    check_rows(w, pool, out, lse, range(96), "sparse prefill-reduced")
 
 
-def test_config3_sparse_prefill_full_sampled():
-    say("fwd config3 full (T=4096, N=131072), sampled rows")
+def test_sparse_prefill_full_sampled():
+    say("fwd sparse prefill full (T=4096, N=131072), sampled rows")
     w = workloads.sparse_prefill()
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
@@ -117,34 +117,34 @@ def test_config3_sparse_prefill_full_sampled():
     empty = [t for t in range(w.num_tokens) if np.all(ind[indptr[t]:indptr[t + 1]] < 0)]
     assert len(empty) == 41
     rows = sorted(set([0, 1, 777, 2048, 3333, 4095] + empty[:2]))
-    check_rows(w, pool, out, lse, rows, "config3-full")
+    check_rows(w, pool, out, lse, rows, "sparse prefill-full")
 
 
-def test_config4_long_context_reduced():
-    say("fwd config4 reduced (T=3, N=20000): automatic split-KV")
+def test_long_context_reduced():
+    say("fwd long context reduced (T=3, N=20000): automatic split-KV")
     w = workloads.long_context(tokens=3, records=20000)
     assert mla.split_workgroups(3, w.nnz, torch.cuda.get_device_properties(0).multi_processor_count) > 0
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
-    check_rows(w, pool, out, lse, range(3), "config4-reduced")
+    check_rows(w, pool, out, lse, range(3), "long context-reduced")
 
 
-def test_config4_long_context_full_sampled():
-    say("fwd config4 full (T=8, N=131072), 2 sampled rows")
+def test_long_context_full_sampled():
+    say("fwd long context full (T=8, N=131072), 2 sampled rows")
     w = workloads.long_context()
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
     check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, [0, 5], "config4-full")
+    check_rows(w, pool, out, lse, [0, 5], "long context-full")
 
 
-def test_config5_insert_attend_full_sampled():
-    say("fwd config5 full: insert then attend, 12 sampled rows")
+def test_insert_attend_full_sampled():
+    say("fwd insert + attend full: insert then attend, 12 sampled rows")
     w = workloads.insert_attend()
     pool, view = build_gpu_pool(w)
     out, lse = run_gpu(w, view)
     check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, list(range(0, 1024, 93)), "config5-full")
+    check_rows(w, pool, out, lse, list(range(0, 1024, 93)), "insert + attend-full")
 
 
 # ----------------------------------------------------------------- sweeps and edges

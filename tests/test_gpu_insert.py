@@ -61,8 +61,8 @@ def test_insert_pool_views_and_strided_inputs(view):
     assert np.array_equal(base.view(512, 656).cpu().numpy(), want)
 
 
-def test_insert_config5_pool_bit_exact():
-    say("insert config5 full pool")
+def test_insert_attend_pool_bit_exact():
+    say("insert: the insert + attend workload's full pool")
     w = workloads.insert_attend()
     pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=DEV)
     for b in w.setup_inserts + w.step_inserts:
