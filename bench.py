@@ -2,7 +2,8 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                 [--no-cpu-baseline] [--copy-calibration]
-                [--epilogue | --prefill-epilogue | --gather | --vproj | --decode-step | --with-sink-extra]
+                [--epilogue | --prefill-epilogue | --gather | --vproj | --insert | --decode-step |
+                 --with-sink-extra]
 
 A step is one pass of the hot path over the workload: for the sparse top-k
 prefill workload (the default) that is one mla_sparse_fwd call over all
@@ -12,11 +13,11 @@ decode epilogue call (mla_decode_q_concat_insert: 4096 tokens, 16 heads,
 RoPE), and with --gather one context-chunk gather + upconvert
 (mla_gather_upconvert: 64 requests of 1024..8192 tokens), and with --vproj
 one W_UV up-projection with the sigmoid gate (mla_v_up_proj: 4096 rows x 16
-heads).  With --decode-step a step is one decode step of 64 requests over
-the paged decode workload (decode epilogue, split-KV forward, gated
-up-projection), timed eagerly and as a replayed HIP graph.  Inputs are
-synthetic, seeded, and resident in HBM before timing starts.  Prints ONE
-JSON line.
+heads); with --insert one cache insert of 131072 tokens.  With --decode-step
+a step is one decode step of 64 requests over the paged decode workload
+(decode epilogue, split-KV forward, gated up-projection), timed eagerly and
+as replayed HIP graphs.  Inputs are synthetic, seeded, and resident in HBM
+before timing starts.  Prints ONE JSON line.
 """
 
 import argparse
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--with-sink-extra", action="store_true",
                     help="forward variant: add per-head sink logits and a second segment of 256 entries per row "
                          "over a second 16384-record pool (mla_sparse_fwd_ex)")
+    ap.add_argument("--insert", action="store_true",
+                    help="measure the cache insert alone: 131072 tokens into random slots of a 131072-record pool")
     ap.add_argument("--decode-step", action="store_true",
                     help="measure one decode step on the paged decode workload (decode epilogue with RoPE and "
                          "insert, split-KV forward, gated up-projection), eager and as a replayed HIP graph")
@@ -120,6 +123,9 @@ def main():
         return
     if args.decode_step:
         bench_decode_step(args, dev)
+        return
+    if args.insert:
+        bench_insert(args, dev)
         return
     log(f"generating workload {args.config}")
     w = workloads.WORKLOADS[args.config]()
@@ -539,6 +545,72 @@ def bench_vproj(args, dev):
         result["cpu_baseline"] = {"value": t / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
                                   "sample": f"the whole call ({t} rows x {h} heads), numpy float64 oracle, "
                                             f"one thread, {el:.2f} s"}
+    print(json.dumps(result), flush=True)
+
+
+def bench_insert(args, dev):
+    """One mla_cache_insert per step: 131072 tokens of [kv_c_normed | k_pe]
+    (N(0,1) bf16) into distinct random slots of a 131072-record pool, 5% of
+    the tokens skipped (slot -1)."""
+    import numpy as np
+    import torch
+
+    import head_latent_attention_sparse_amd as mla
+
+    log("generating the insert inputs")
+    n, records = 131072, 131072
+    g = torch.Generator().manual_seed(20261202 + 11)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    slots = torch.randperm(records, generator=g)[:n]
+    slots[torch.rand(n, generator=g) < 0.05] = -1
+    kv, pe, sl = kv_c.to(dev), k_pe.to(dev), slots.to(dev)
+    pool = torch.zeros((records, 656), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        mla.cache_insert(kv, pe, sl, pool)
+
+    ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
+    written = int((slots >= 0).sum())
+    moved = n * (512 * 2 + 64 * 2 + 8) + written * 656  # tokens and slots read, records written
+    achieved = moved / (dev_ms * 1e-3) / 1e9
+    result = {
+        "metric": "fp8_ds_mla cache insert: tokens/s",
+        "value": n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"cache insert: {n} tokens into random slots of a {records}-record pool, 5% skipped",
+                   "parallelism": "single GPU"},
+        "device_ms_per_step": dev_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
+    }
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import encode_records
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        keep = slots.numpy() >= 0
+        kb, pb = bf16_bits(kv_c)[keep], bf16_bits(k_pe)[keep]
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            recs = encode_records(kb, pb)
+            el = time.perf_counter() - t0
+        assert recs.shape == (int(keep.sum()), 656) and np.isfinite(el)
+        result["cpu_baseline"] = {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole call ({int(keep.sum())} records written, {n} tokens), "
+                                            f"numpy oracle writer, one thread, {el:.2f} s"}
     print(json.dumps(result), flush=True)
 
 
