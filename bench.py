@@ -500,11 +500,16 @@ def bench_vproj(args, dev):
     lat, wuv, gate = w.latent.to(dev), w.w_uv.to(dev), w.gate.to(dev)
     t, h = lat.shape[0], lat.shape[1]
     out = torch.empty((t, h, 128), dtype=torch.bfloat16, device=dev)
+    prepared = mla.prepare_w_uv(wuv)  # once, as after loading the weights
     torch.cuda.synchronize()
 
     def step():
+        mla.v_up_proj(lat, prepared, gate=gate, out=out, prepared=True)
+
+    def step_plain():
         mla.v_up_proj(lat, wuv, gate=gate, out=out)
 
+    _, plain_dev_ms = time_steps(step_plain, args, torch.cuda.current_stream(dev))
     ms, dev_ms = time_steps(step, args, torch.cuda.current_stream(dev))
     moved = lat.numel() * 2 + wuv.numel() * 2 + gate.numel() * 2 + out.numel() * 2
     flops = 2.0 * t * h * 512 * 128
@@ -525,12 +530,14 @@ def bench_vproj(args, dev):
         "config": {"workload": f"v up-projection: T={t} rows, H={h}, latent 512 -> v 128, gated",
                    "parallelism": "single GPU"},
         "device_ms_per_step": dev_ms,
+        "weights": "prepared once with mla_v_up_proj_prepare_weights (outside the timed steps)",
+        "plain_weights_device_ms_per_step": plain_dev_ms,
         "mfma_tflops": flops / (dev_ms * 1e-3) / 1e12,
         "mfma_frac": flops / (dev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
     }
-    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms)")
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (device {dev_ms:.4f} ms; plain weights {plain_dev_ms:.4f} ms)")
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
 
@@ -637,7 +644,7 @@ def bench_decode_step(args, dev):
     ql, qp, kv, kp = e.ql_nope.to(dev), e.q_pe.to(dev), e.kv_c.to(dev), e.k_pe.to(dev)
     slots, pos, table = e.slots.to(dev), e.positions.to(dev), e.cos_sin_cache.to(dev)
     vp = workloads.v_up_proj_inputs(tokens=b, heads=h)
-    w_uv, gate = vp.w_uv.to(dev), vp.gate.to(dev)
+    w_uv, gate = mla.prepare_w_uv(vp.w_uv.to(dev)), vp.gate.to(dev)  # prepared once, as after loading
     indptr, indices = w.indptr.to(dev), w.indices.to(dev)
     mqa = torch.empty((b, h, 576), dtype=torch.bfloat16, device=dev)
     out = torch.empty((b, h, 512), dtype=torch.bfloat16, device=dev)
@@ -649,7 +656,7 @@ def bench_decode_step(args, dev):
     def step():
         mla.decode_q_concat_insert(ql, qp, kv, kp, view, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
         mla.sparse_fwd(mqa, view, indptr, indices, w.softmax_scale, out=out, return_lse=True, workspace=workspace)
-        mla.v_up_proj(out, w_uv, gate=gate, out=vout)
+        mla.v_up_proj(out, w_uv, gate=gate, out=vout, prepared=True)
 
     stream = torch.cuda.current_stream(dev)
     eager_ms, eager_dev = time_steps(step, args, stream)

@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     gather_upconvert,
     key_concat_insert,
     lib,
+    prepare_w_uv,
     split_workgroups,
     sparse_fwd,
     v_up_proj,

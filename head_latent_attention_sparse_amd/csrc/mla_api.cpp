@@ -476,11 +476,12 @@ mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, i
   return MLA_OK;
 }
 
-mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
-                           const void *w_uv, const void *gate, int64_t gate_stride_token, int64_t num_tokens,
-                           int32_t num_heads, void *out, int64_t out_stride_token, int64_t out_stride_head,
-                           void *stream) {
-  const char *fn = "mla_v_up_proj";
+namespace {
+
+mla_status_t v_up_proj_impl(const char *fn, bool prepared, const void *latent, int64_t latent_stride_token,
+                            int64_t latent_stride_head, const void *w_uv, const void *gate,
+                            int64_t gate_stride_token, int64_t num_tokens, int32_t num_heads, void *out,
+                            int64_t out_stride_token, int64_t out_stride_head, void *stream) {
   if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_tokens %lld < 0", fn, (long long)num_tokens);
   if (num_heads < 1 || num_heads > MLA_MAX_EPILOGUE_HEADS)
     return fail(MLA_ERR_UNSUPPORTED, "%s: num_heads %d outside 1..%d", fn, num_heads, MLA_MAX_EPILOGUE_HEADS);
@@ -489,7 +490,7 @@ mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int6
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative stride", fn);
   if (!aligned(latent, 16) || latent_stride_token % 8 || latent_stride_head % 8)
     return fail(MLA_ERR_UNSUPPORTED, "%s: latent must be 16-byte aligned with strides that are multiples of 8", fn);
-  if (!aligned(out, 4) || (out_stride_token | out_stride_head) & 1 || !aligned(w_uv, 2) ||
+  if (!aligned(out, 4) || (out_stride_token | out_stride_head) & 1 || !aligned(w_uv, prepared ? 16 : 2) ||
       (gate && (!aligned(gate, 4) || (gate_stride_token & 1))))
     return fail(MLA_ERR_UNSUPPORTED, "%s: out / gate must be 4-byte aligned with even strides", fn);
   if (num_tokens == 0) return MLA_OK;
@@ -508,7 +509,43 @@ mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int6
   a.out = static_cast<uint16_t *>(out);
   a.out_st = out_stride_token;
   a.out_sh = out_stride_head;
+  a.w_prepared = prepared;
   hipError_t e = mla::launch_v_up_proj(a, device_cus(device), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
+                           const void *w_uv, const void *gate, int64_t gate_stride_token, int64_t num_tokens,
+                           int32_t num_heads, void *out, int64_t out_stride_token, int64_t out_stride_head,
+                           void *stream) {
+  return v_up_proj_impl("mla_v_up_proj", false, latent, latent_stride_token, latent_stride_head, w_uv, gate,
+                        gate_stride_token, num_tokens, num_heads, out, out_stride_token, out_stride_head, stream);
+}
+
+mla_status_t mla_v_up_proj_prepared(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
+                                    const void *w_prepared, const void *gate, int64_t gate_stride_token,
+                                    int64_t num_tokens, int32_t num_heads, void *out, int64_t out_stride_token,
+                                    int64_t out_stride_head, void *stream) {
+  return v_up_proj_impl("mla_v_up_proj_prepared", true, latent, latent_stride_token, latent_stride_head, w_prepared,
+                        gate, gate_stride_token, num_tokens, num_heads, out, out_stride_token, out_stride_head,
+                        stream);
+}
+
+mla_status_t mla_v_up_proj_prepare_weights(const void *w_uv, int32_t num_heads, void *w_prepared, void *stream) {
+  const char *fn = "mla_v_up_proj_prepare_weights";
+  if (num_heads < 1 || num_heads > MLA_MAX_EPILOGUE_HEADS)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: num_heads %d outside 1..%d", fn, num_heads, MLA_MAX_EPILOGUE_HEADS);
+  if (!w_uv || !w_prepared) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL w_uv or w_prepared", fn);
+  if (!aligned(w_uv, 2) || !aligned(w_prepared, 16))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: w_uv must be 2-byte and w_prepared 16-byte aligned", fn);
+  const char *a = static_cast<const char *>(w_uv), *b = static_cast<const char *>(w_prepared);
+  const int64_t bytes = (int64_t)num_heads * MLA_KV_LORA_RANK * 128 * 2;
+  if (a < b + bytes && b < a + bytes) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: w_uv and w_prepared overlap", fn);
+  hipError_t e = mla::launch_prepare_w_uv(static_cast<const uint16_t *>(w_uv), static_cast<uint16_t *>(w_prepared),
+                                          num_heads, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return MLA_OK;
 }

@@ -132,9 +132,12 @@ struct VUpProjArgs {
   int32_t num_heads;
   uint16_t *out;           // bf16, element (t, h, v) at t*out_st + h*out_sh + v
   int64_t out_st, out_sh;
+  bool w_prepared = false;  // w holds launch_prepare_w_uv's fragment order
 };
 
 hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t stream);
+// W_UV [H, 512, 128] bf16 -> the same bytes in the up-projection's fragment order
+hipError_t launch_prepare_w_uv(const uint16_t *w, uint16_t *w_prepared, int32_t num_heads, hipStream_t stream);
 
 // Workspace of a chunked (split-KV) call, in 256-byte aligned parts:
 // partials, partial LSEs, row prefix.

@@ -28,6 +28,7 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;           // wave w owns output columns 32w .. 32w+31
 constexpr int kV = 128;                          // v_head_dim
 constexpr int kTileRows = 32;
 constexpr int kKSteps = kLatent / 32;            // 16 MFMA k-steps of 32
@@ -48,7 +49,7 @@ struct TileRegs {
   u32x4_t gate[kOutChunks];
 };
 
-template <bool kGate>
+template <bool kGate, bool kPrepared>
 __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   uint16_t *s_a = reinterpret_cast<uint16_t *>(smem);
@@ -98,7 +99,15 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
   // coalesced 16-byte loads into LDS (pitch 264 B: the 4 row groups of a
   // read land 16 banks apart), then 2-byte reads down the columns.
   bf16x8_t bw[kKSteps][2];
-  {
+  if (kPrepared) {
+    // the fragments in the order prepare_w_uv_kernel wrote them: one
+    // 16-byte load each, no staging
+    const u32x4_t *wp = reinterpret_cast<const u32x4_t *>(a.w) + ((int64_t)h * kWaves + wave) * (kKSteps * 2 * 64);
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bw[s][j] = as_bf16x8(wp[(s * 2 + j) * 64 + lane]);
+  } else {
     const uint16_t *w = a.w + (int64_t)h * kLatent * kV;
     u32x4_t wr[kLatent / kWRows][8];  // every pass's loads in flight at once
 #pragma unroll
@@ -235,6 +244,28 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
   }
 }
 
+// W_UV in the kernel's B-fragment order: fragment (h, w, s, j) of lane
+// (c, g) = rows 32s + 8g .. +7 of column 32w + 16j + c of W_UV[h], 8 bf16
+// values (row order, the first in the low half), stored as 16 bytes at
+// index ((((h * 4 + w) * 16 + s) * 2 + j) * 64 + lane).  One thread per
+// fragment.
+__global__ __launch_bounds__(256) void prepare_w_uv_kernel(const uint16_t *w, uint16_t *wp, int64_t fragments) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= fragments) return;
+  const int lane = (int)(f & 63), c = lane & 15, g = lane >> 4;
+  const int j = (int)((f >> 6) & 1);
+  const int s = (int)((f >> 7) & (kKSteps - 1));
+  const int64_t hw = f >> 11;  // h * 4 + wave
+  const int wave = (int)(hw & 3);
+  const int64_t h = hw >> 2;
+  const uint16_t *col = w + h * kLatent * kV + (int64_t)(32 * s + 8 * g) * kV + 32 * wave + 16 * j + c;
+  uint32_t v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (uint32_t)col[(2 * e) * kV] | ((uint32_t)col[(2 * e + 1) * kV] << 16);
+  *reinterpret_cast<u32x4_t *>(wp + f * 8) = u32x4_t{v[0], v[1], v[2], v[3]};
+}
+static_assert(kKSteps == 16 && kWaves == 4, "fragment index layout");
+
 }  // namespace
 
 hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t stream) {
@@ -243,10 +274,23 @@ hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t strea
   int64_t per_head = (num_cus > 0 ? num_cus : 256) / a.num_heads;
   per_head = per_head < 1 ? 1 : (per_head > tiles ? tiles : per_head);
   const dim3 grid((unsigned)per_head, (unsigned)a.num_heads);
-  if (a.gate)
-    v_up_proj_kernel<true><<<grid, dim3(kThreads), 0, stream>>>(a);
-  else
-    v_up_proj_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  if (a.w_prepared) {
+    if (a.gate)
+      v_up_proj_kernel<true, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+    else
+      v_up_proj_kernel<false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  } else {
+    if (a.gate)
+      v_up_proj_kernel<true, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+    else
+      v_up_proj_kernel<false, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_w_uv(const uint16_t *w, uint16_t *w_prepared, int32_t num_heads, hipStream_t stream) {
+  const int64_t fragments = (int64_t)num_heads * kLatent * kV / 8;
+  prepare_w_uv_kernel<<<dim3((unsigned)((fragments + 255) / 256)), dim3(256), 0, stream>>>(w, w_prepared, fragments);
   return hipGetLastError();
 }
 

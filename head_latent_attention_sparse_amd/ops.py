@@ -48,6 +48,8 @@ SIGNATURES = {
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
     "mla_cache_insert": (_I32, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I64, _P]),
     "mla_v_up_proj": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _I64, _I64, _P]),
+    "mla_v_up_proj_prepared": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _I64, _I64, _P]),
+    "mla_v_up_proj_prepare_weights": (_I32, [_P, _I32, _P, _P]),
     "mla_gather_upconvert": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _I64, _P, _P, _I32, _I64, _P, _I64, _P]),
     "mla_prefill_key_concat_insert": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64,
                                              _I32, _P, _P, _I64, _P, _I64, _I64, _P, _I64, _I64, _P]),
@@ -393,12 +395,31 @@ def gather_upconvert(kv_cache, block_table, cu_seq_lens, num_tokens, *, seq_star
 V_HEAD_DIM = 128
 
 
-def v_up_proj(latent, w_uv, *, gate=None, out=None):
+def prepare_w_uv(w_uv):
+    """W_UV bf16 [H, 512, 128] -> the same values in the up-projection's
+    fragment order (a bf16 tensor of the same shape whose layout is internal:
+    pass it to v_up_proj with prepared=True).  Done once, after loading."""
+    if not (torch.is_tensor(w_uv) and w_uv.is_cuda and w_uv.dtype == torch.bfloat16 and w_uv.ndim == 3
+            and tuple(w_uv.shape[1:]) == (KV_LORA_RANK, V_HEAD_DIM) and w_uv.is_contiguous()):
+        raise ValueError("w_uv must be a contiguous CUDA bf16 [H, 512, 128] tensor")
+    heads = w_uv.shape[0]
+    if not 1 <= heads <= MAX_EPILOGUE_HEADS:
+        raise ValueError(f"{heads} heads: 1 .. {MAX_EPILOGUE_HEADS} are served")
+    dev = w_uv.device
+    prepared = torch.empty_like(w_uv)
+    with torch.cuda.device(dev):
+        st = lib().mla_v_up_proj_prepare_weights(w_uv.data_ptr(), heads, prepared.data_ptr(), _stream(dev))
+    _check(st)
+    return prepared
+
+
+def v_up_proj(latent, w_uv, *, gate=None, out=None, prepared=False):
     """out[t, h, :] = latent[t, h, :512] @ w_uv[h] (times sigmoid(gate)) -> bf16 [T, H, 128].
 
     latent: bf16 [T, H, >= 512] (e.g. sparse_fwd's out) with a contiguous last
-    dim, 16-byte aligned rows; w_uv: bf16 [H, 512, 128] contiguous; gate:
-    bf16 [T, H * 128] with a contiguous last dim, or None.
+    dim, 16-byte aligned rows; w_uv: bf16 [H, 512, 128] contiguous (or, with
+    prepared=True, prepare_w_uv's result for it); gate: bf16 [T, H * 128]
+    with a contiguous last dim, or None.
     """
     if not (torch.is_tensor(latent) and latent.is_cuda and latent.dtype == torch.bfloat16 and latent.ndim == 3
             and latent.shape[2] >= KV_LORA_RANK and latent.stride(2) == 1):
@@ -420,9 +441,10 @@ def v_up_proj(latent, w_uv, *, gate=None, out=None):
         raise ValueError("out must be bf16 [T, H, >= 128] with a contiguous last dim")
     L = lib()
     with torch.cuda.device(dev):
-        st = L.mla_v_up_proj(latent.data_ptr(), latent.stride(0), latent.stride(1), w_uv.data_ptr(),
-                             gate.data_ptr() if gate is not None else None, gate.stride(0) if gate is not None else 0,
-                             t_count, heads, out.data_ptr(), out.stride(0), out.stride(1), _stream(dev))
+        fn = L.mla_v_up_proj_prepared if prepared else L.mla_v_up_proj
+        st = fn(latent.data_ptr(), latent.stride(0), latent.stride(1), w_uv.data_ptr(),
+                gate.data_ptr() if gate is not None else None, gate.stride(0) if gate is not None else 0,
+                t_count, heads, out.data_ptr(), out.stride(0), out.stride(1), _stream(dev))
     _check(st)
     return out
 

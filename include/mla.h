@@ -361,6 +361,32 @@ mla_status_t mla_v_up_proj(const void *latent, int64_t latent_stride_token, int6
                            int32_t num_heads, void *out, int64_t out_stride_token, int64_t out_stride_head,
                            void *stream);
 
+/*
+ * mla_v_up_proj_prepare_weights - W_UV in the up-projection's own order,
+ * once, after the weights are loaded (the page's
+ * process_weights_after_loading prepares W_UV from kv_b_proj at the same
+ * point).  Writes num_heads * 512 * 128 * 2 bytes to w_prepared: the same
+ * values, laid out as the matrix-core fragments mla_v_up_proj_prepared
+ * loads directly (an internal order: use the buffer only with that call and
+ * the same num_heads).
+ *
+ *  w_uv         bf16 [num_heads, 512, 128] contiguous, 2-byte aligned.
+ *  num_heads    1 .. MLA_MAX_EPILOGUE_HEADS.
+ *  w_prepared   num_heads * 131072 bytes, 16-byte aligned, not overlapping w_uv.
+ */
+mla_status_t mla_v_up_proj_prepare_weights(const void *w_uv, int32_t num_heads, void *w_prepared, void *stream);
+
+/*
+ * mla_v_up_proj_prepared - mla_v_up_proj with the weights from
+ * mla_v_up_proj_prepare_weights: the same results bit for bit, without the
+ * per-call weight transposition.  Arguments as for mla_v_up_proj, with
+ * w_prepared (16-byte aligned) in place of w_uv.
+ */
+mla_status_t mla_v_up_proj_prepared(const void *latent, int64_t latent_stride_token, int64_t latent_stride_head,
+                                    const void *w_prepared, const void *gate, int64_t gate_stride_token,
+                                    int64_t num_tokens, int32_t num_heads, void *out, int64_t out_stride_token,
+                                    int64_t out_stride_head, void *stream);
+
 /* Message for the last failed call on this thread ("" if none).  Host memory
  * owned by the library, valid until the thread's next failing call. */
 const char *mla_last_error(void);
@@ -369,7 +395,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 7
+#define MLA_ABI_VERSION 8
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

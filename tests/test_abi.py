@@ -235,12 +235,12 @@ def test_gather_zero_tokens_is_a_no_op():
     assert st == OK
 
 
-def vproj(**kw):
+def vproj(prepared=False, **kw):
     args = dict(lat=A, lst=16 * 512, lsh=512, w=A, gate=None, gst=0, T=64, H=16, out=A, ost=16 * 128, osh=128,
                 stream=None)
     args.update(kw)
     lib = mla.lib()
-    st = lib.mla_v_up_proj(*args.values())
+    st = (lib.mla_v_up_proj_prepared if prepared else lib.mla_v_up_proj)(*args.values())
     return st, lib.mla_last_error().decode()
 
 
@@ -267,6 +267,33 @@ def test_v_up_proj_rejections(kw, status):
 def test_v_up_proj_zero_tokens_is_a_no_op():
     st, _ = vproj(T=0, lat=None, w=None, out=None)
     assert st == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=0), UNSUPPORTED),
+    (dict(w=A + 2), UNSUPPORTED),  # prepared weights are read 16 bytes at a time
+    (dict(w=None), INVALID),
+    (dict(lat=A + 8), UNSUPPORTED),
+])
+def test_v_up_proj_prepared_rejections(kw, status):
+    st, msg = vproj(prepared=True, **kw)
+    assert st == status, msg
+    assert msg
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 0, A + (1 << 24), None), UNSUPPORTED),
+    ((A, 1025, A + (1 << 30), None), UNSUPPORTED),
+    ((None, 16, A, None), INVALID),
+    ((A, 16, None, None), INVALID),
+    ((A, 16, A + 8 + (1 << 24), None), UNSUPPORTED),  # output not 16-byte aligned
+    ((A, 16, A + 4096, None), INVALID),  # overlapping buffers
+])
+def test_prepare_weights_rejections(args, status):
+    lib = mla.lib()
+    st = lib.mla_v_up_proj_prepare_weights(*args)
+    assert st == status, lib.mla_last_error().decode()
+    assert lib.mla_last_error()
 
 
 def fwd_ex(**kw):

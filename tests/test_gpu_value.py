@@ -73,3 +73,24 @@ def test_v_up_proj_empty_and_rejections():
     with pytest.raises(ValueError):  # rows not 16-byte aligned
         base = torch.zeros((3 * 4 * 516 + 4,), dtype=torch.bfloat16, device=DEV)
         mla.v_up_proj(base[4:].view(3, 4, 516)[:, :, :512], wuv)
+
+
+@pytest.mark.parametrize("t,h", [(1, 1), (64, 16), (300, 12), (129, 128), (4096, 16)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_v_up_proj_prepared_weights(t, h, gated):
+    """mla_v_up_proj_prepared on mla_v_up_proj_prepare_weights' layout gives
+    mla_v_up_proj's results bit for bit (and so meets the oracle's bar), and
+    the preparation leaves W_UV untouched."""
+    say(f"v_up_proj prepared T={t} H={h} gate={gated}")
+    w = workloads.v_up_proj_inputs(tokens=t, heads=h)
+    lat, wuv = w.latent.to(DEV), w.w_uv.to(DEV)
+    gate = w.gate.to(DEV) if gated else None
+    prepared = mla.prepare_w_uv(wuv)
+    got = mla.v_up_proj(lat, prepared, gate=gate, prepared=True)
+    plain = mla.v_up_proj(lat, wuv, gate=gate)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), plain.view(torch.int16)), "prepared path differs from the plain one"
+    assert torch.equal(wuv.cpu(), w.w_uv), "W_UV changed"
+    assert not torch.equal(prepared.cpu(), w.w_uv) or h * t == 0, "the prepared layout is a different order"
+    if t <= 300:
+        check(got, oracle_v_up_proj(bf16_bits(w.latent), bf16_bits(w.w_uv), bf16_bits(w.gate) if gated else None))
