@@ -1,6 +1,6 @@
 """The entry points under HIP graph capture (torch.cuda.graph): a decode
 step (epilogue with RoPE and insert -> split-KV forward -> W_UV
-up-projection with gate) and a prefill step (key epilogue with q RoPE in
+up-projection with gate, with plain and prepared weights) and a prefill step (key epilogue with q RoPE in
 place and insert -> plain insert -> one-workgroup-per-row forward, int64
 indices -> context gather through a block table), each
 captured once and replayed several times.  Before each replay the program
@@ -102,6 +102,8 @@ def test_decode_step_graph():
     out = torch.empty((b, h, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((b, h), dtype=torch.float32, device=DEV)
     vout = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
+    w_prep = mla.prepare_w_uv(w_uv)  # once, before capture
+    vout_p = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
     assert mla.split_workgroups(b, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count) > 0
 
     def fresh(r):
@@ -118,9 +120,11 @@ def test_decode_step_graph():
         _, l = mla.sparse_fwd(mqa, pool, ip, ix, SCALE, has_invalid=True, out=out, return_lse=True)
         lse.copy_(l)
         mla.v_up_proj(out, w_uv, gate=gate, out=vout)
+        mla.v_up_proj(out, w_prep, gate=gate, out=vout_p, prepared=True)
 
     check_replays(step, [ql, qp, kv, kp, slots, pos, ix, gate], lambda r: [x.to(DEV) for x in fresh(r)],
-                  [mqa, out, lse, vout], pool)
+                  [mqa, out, lse, vout, vout_p], pool)
+    assert torch.equal(vout.view(torch.int16), vout_p.view(torch.int16))
 
 
 def test_prefill_step_graph():
