@@ -135,3 +135,31 @@ def test_row_start_guess(layout, split):
     out, lse = run(q, rec, ptr, idx, dtype)
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
     assert_fwd_close(out, lse, ref_out, ref_lse, f"guess {layout} split={split}")
+
+
+@pytest.mark.parametrize("t", [8, 64])
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_split_without_lse(t, with_sink):
+    """The split pass and merge when no LSE is asked for (the merge then
+    writes out only), with and without a sink, at both merge shapes the
+    row counts pick; out against the oracle."""
+    say(f"split without lse T={t} sink={with_sink}")
+    g = torch.Generator().manual_seed(80 + t)
+    n = 4096
+    q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
+    lens = torch.randint(600, 3000, (t,), generator=g).numpy().astype(np.int64)
+    ptr = np.concatenate([[0], np.cumsum(lens)])
+    idx = torch.randint(-1, n, (int(ptr[-1]),), generator=g).numpy().astype(np.int64)
+    sink = (torch.randn((16,), generator=g) * 2).numpy().astype(np.float32) if with_sink else None
+    assert mla.split_workgroups(t, idx.size, torch.cuda.get_device_properties(0).multi_processor_count) > 0
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out, lse = mla.sparse_fwd(dev(bf16_bits(q)).view(torch.bfloat16), dev(rec), dev(ptr).to(torch.int32),
+                              dev(idx).to(torch.int32), SCALE, has_invalid=True, return_lse=False,
+                              attn_sink=dev(sink) if with_sink else None)
+    torch.cuda.synchronize()
+    assert lse is None
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE, sink=sink)
+    assert_fwd_close(out, None, ref_out, ref_lse, f"split without lse T={t}")
