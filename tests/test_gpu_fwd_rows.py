@@ -137,11 +137,11 @@ def test_row_start_guess(layout, split):
     assert_fwd_close(out, lse, ref_out, ref_lse, f"guess {layout} split={split}")
 
 
-@pytest.mark.parametrize("t", [8, 64])
+@pytest.mark.parametrize("t", [8, 20, 64])
 @pytest.mark.parametrize("with_sink", [False, True])
 def test_split_without_lse(t, with_sink):
     """The split pass and merge when no LSE is asked for (the merge then
-    writes out only), with and without a sink, at both merge shapes the
+    writes out only), with and without a sink, at the three merge shapes the
     row counts pick; out against the oracle."""
     say(f"split without lse T={t} sink={with_sink}")
     g = torch.Generator().manual_seed(80 + t)

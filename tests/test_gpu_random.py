@@ -3,8 +3,8 @@ with the forward's bar.  Each seed draws a whole problem: rows T in [1, 700],
 heads H in [1, 16], a pool of up to 4096 records, row lengths from one of
 four mixes (short, long, mixed with empty rows, equal rows back to back),
 masked and out-of-pool entries, int32 or int64 indices, the library's plan
-or forced chunks, padded strides for q and out, and (for some seeds) a sink
-and a second segment.  The draws combine cases the targeted tests cover one
+or forced chunks, with or without the LSE, padded strides for q and out,
+and (for some seeds) a sink and a second segment.  The draws combine cases the targeted tests cover one
 at a time; the seeds are fixed, so a failure names a reproducible problem.
 """
 
@@ -54,6 +54,7 @@ def draw(seed):
              chunk_tiles=int(rng.choice([0, 0, 1, 3, 8])) if t <= 512 else 0,
              scale=float(rng.choice([192 ** -0.5, 0.02, 0.2])),
              q_pad=int(rng.choice([0, 8, 64])), o_pad=int(rng.choice([0, 8, 100])))
+    p["return_lse"] = bool(rng.random() < 0.7)  # drawn after the rest: earlier draws are unchanged
     if seed % 3 == 2:  # sink and second segment
         n2 = int(rng.integers(1, 1025))
         kv2 = torch.randn((n2, 512), generator=g).to(torch.bfloat16)
@@ -70,7 +71,7 @@ def draw(seed):
 def test_random_problem(seed):
     p = draw(seed)
     say(f"random seed {seed}: {p['mix']} T={p['t']} H={p['h']} N={p['n']} nnz={p['idx'].size} "
-        f"{p['dtype']} chunk_tiles={p['chunk_tiles']} extra={'rec2' in p}")
+        f"{p['dtype']} chunk_tiles={p['chunk_tiles']} extra={'rec2' in p} lse={p['return_lse']}")
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     t, h = p["t"], p["h"]
     qbuf = torch.zeros((t, h, 576 + p["q_pad"]), dtype=torch.bfloat16, device=DEV)
@@ -82,11 +83,13 @@ def test_random_problem(seed):
                      extra_indices=dev(p["idx2"]).to(p["dtype"]), attn_sink=dev(p["sink"]))
     out, lse = mla.sparse_fwd(qbuf[:, :, :576], dev(p["rec"]), dev(p["ptr"]).to(p["dtype"]),
                               dev(p["idx"]).to(p["dtype"]), p["scale"], has_invalid=True,
-                              out=obuf[:, :, :512], return_lse=True, chunk_tiles=p["chunk_tiles"], **extra)
+                              out=obuf[:, :, :512], return_lse=p["return_lse"], chunk_tiles=p["chunk_tiles"],
+                              **extra)
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_fwd(bf16_bits(p["q"]), p["rec"], p["ptr"], p["idx"], p["scale"],
                                   extra=(p["rec2"], p["ptr2"], p["idx2"]) if "rec2" in p else None,
                                   sink=p.get("sink"))
+    assert (lse is None) == (not p["return_lse"])
     assert_fwd_close(out, lse, ref_out, ref_lse, f"seed {seed}")
     if p["o_pad"]:
         assert torch.all(obuf[:, :, 512:].cpu() == -3.0), "columns past 512 were written"
