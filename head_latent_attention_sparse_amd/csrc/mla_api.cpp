@@ -47,9 +47,15 @@ int device_cus(int device) {
   return cache[device];
 }
 
+// The library-owned split workspace of one device.  A buffer that is
+// replaced by a larger one is retired, not freed: work queued earlier (or
+// a graph captured earlier) may still name it, so it stays allocated until
+// the process ends.  Growth at least doubles, so the retired buffers
+// together stay smaller than the current one.
 struct Workspace {
   void *ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void *> retired;
 };
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
@@ -63,21 +69,18 @@ mla_status_t workspace_get(int device, size_t bytes, void **out) {
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed");
     if (prev != device && hipSetDevice(device) != hipSuccess) return fail(MLA_ERR_HIP, "hipSetDevice(%d) failed", device);
-    if (w.ptr) {
-      // hipFree waits for work that may still use the old buffer.
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    const size_t want = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
-    hipError_t e = hipMalloc(&w.ptr, want);
+    const size_t grown = bytes > 2 * w.bytes ? bytes : 2 * w.bytes;
+    const size_t want = (grown + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+    void *fresh = nullptr;
+    hipError_t e = hipMalloc(&fresh, want);
     if (prev != device) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
-      w.ptr = nullptr;
       (void)hipGetLastError();
       return fail(MLA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated on device %d: %s", want,
                   device, hipGetErrorString(e));
     }
+    if (w.ptr) w.retired.push_back(w.ptr);
+    w.ptr = fresh;
     w.bytes = want;
   }
   *out = w.ptr;

@@ -17,8 +17,9 @@
 //    The latent part runs on the records' E4M3 codes as they are, with the
 //    block-scaled fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the query is
 //    split once per row into two E4M3 terms with power-of-two block scales
-//    (hi + lo, about 2^-19 relative to its 32-element group's max), and each
-//    key's per-128 tile scale multiplies that tile's float32 partial.  The
+//    (hi + lo: exact except for elements tiny next to their 32-element
+//    group's max, off by at most 2^-18 of that max), and each key's per-128
+//    tile scale multiplies that tile's float32 partial.  The
 //    rope part is a bf16 MFMA;
 //  * the 16x64 logits go through LDS; every wave computes the online-softmax
 //    weights of the whole tile in the exp2 domain (scale * log2 e, as the
@@ -447,9 +448,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   //   y  = x * 2^k,  k = 7 - floor(log2 amax)         (amax * 2^k in [128, 256))
   //   hi = y with its mantissa cut to 3 bits if |y| >= 2^-6, else 0 (exact E4M3)
   //   r  = y - hi (exact);  lo = E4M3(r * 2^k2),  k2 = 7 - floor(log2 max |r|)
-  // so x = hi * 2^-k + lo * 2^-(k+k2): exact when r * 2^k2 is an E4M3 normal,
-  // otherwise off by at most 2^-12 * 2^-k (about 2^-19 of amax).  The two
-  // powers of two are the e8m0 block scales of the A operand.  Staged through
+  // and x ~ hi * 2^-k + lo * 2^-(k+k2).  Where hi != 0, r holds the 4 bits of
+  // y below hi's, so lo is exact unless r * 2^k2 falls below E4M3's normal
+  // range (error <= 2^-10 * 2^-(k+k2), k2 >= 4: at most 2^-21 of amax).
+  // Where hi = 0 (|y| < 2^-6), r = y keeps bf16's 8 significant bits and lo
+  // rounds it to 4: error <= 2^-4 * 2^-7 * 2^-k, at most 2^-18 of amax
+  // (for amax >= 2^-119, where k is not capped).  The
+  // two powers of two are the e8m0 block scales of the A operand.  Staged through
   // the tile buffer before its first use: wave w splits latent tile w, lane
   // (h, kb) = (n, g) one group; then every wave reads all four tiles.
   intx8_t qa[4][2];     // [latent tile][hi, lo], MFMA A layout

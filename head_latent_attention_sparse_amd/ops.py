@@ -98,28 +98,35 @@ def _check(status, unsupported_is_value_error=True):
     raise MlaError(status, msg)
 
 
-def _kv_rows(kv):
-    """(base pointer, number of records, record pitch) of a record pool view.
+def _record_pool(kv):
+    """(base pointer, number of records, record pitch in bytes) of a pool view.
 
-    Takes [N, 656], [N, 1, 656], [N, 1, 1, 656] or an unpadded paged pool
-    [nb, block, 656] of any 1-byte dtype (the views the flydsl_sparse_mla
-    page's ``_kv_rows`` accepts).  A layout that is not flat records yields a
-    pitch other than 656, which the library rejects.
+    A pool is any 1-byte tensor of rank 2 to 4 whose last dim holds one
+    656-byte record contiguously, e.g. a flat [N, 656] pool, [N, 1, 656],
+    [N, 1, 1, 656], or a paged pool [num_blocks, block_size, 656].  The
+    dims before the record dim must step through memory as one evenly
+    spaced run (each dim's stride equal to the next inner dim's stride
+    times its size, size-1 dims ignored); the pitch is that run's innermost
+    stride.  A run that is not even (a padded page pitch) gives pitch -1,
+    and the library serves only pitch 656, so both are refused there.
     """
-    if not torch.is_tensor(kv) or kv.element_size() != 1 or kv.ndim not in (2, 3, 4):
+    if not torch.is_tensor(kv) or kv.element_size() != 1 or not 2 <= kv.ndim <= 4:
         raise ValueError("kv cache must be a 1-byte tensor of rank 2, 3 or 4")
     if kv.shape[-1] != RECORD_BYTES or kv.stride(-1) != 1:
         raise ValueError("kv cache rows must be 656 contiguous bytes")
-    if kv.ndim == 4 and (kv.shape[1] != 1 or kv.shape[2] != 1):
-        raise ValueError("a 4-D kv cache must be [N, 1, 1, 656]")
-    n = kv.numel() // RECORD_BYTES
-    if kv.ndim == 3 and kv.shape[1] != 1:
-        pitch = kv.stride(1)
-        if kv.shape[0] > 1 and kv.stride(0) != kv.shape[1] * pitch:
-            pitch = kv.stride(0)  # padded pages: rejected by the library
-    else:
-        pitch = kv.stride(0) if kv.shape[0] > 1 else RECORD_BYTES
-    return kv.data_ptr(), n, pitch
+    count = 1
+    for size in kv.shape[:-1]:
+        count *= size
+    walk = [(size, stride) for size, stride in zip(kv.shape[:-1], kv.stride()[:-1]) if size > 1]
+    if not walk:
+        return kv.data_ptr(), count, RECORD_BYTES
+    pitch = walk[-1][1]
+    span = pitch
+    for size, stride in reversed(walk):
+        if stride != span:
+            return kv.data_ptr(), count, -1
+        span = stride * size
+    return kv.data_ptr(), count, pitch
 
 
 def _stream(device):
@@ -176,14 +183,14 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
             raise ValueError("extra_indptr must have T + 1 entries")
         if not (torch.is_tensor(extra_kv) and extra_kv.device == q.device):
             raise ValueError("extra_kv must be on q's device")
-        ekv_ptr, en_rec, epitch = _kv_rows(extra_kv)
+        ekv_ptr, en_rec, epitch = _record_pool(extra_kv)
     if attn_sink is not None and not (torch.is_tensor(attn_sink) and attn_sink.dtype == torch.float32
                                       and attn_sink.device == q.device and attn_sink.ndim == 1
                                       and attn_sink.numel() == heads and attn_sink.is_contiguous()):
         raise ValueError("attn_sink must be a contiguous float32 [H] tensor on q's device")
     if not (torch.is_tensor(kv_cache) and kv_cache.device == q.device):
         raise ValueError("kv cache must be on q's device")
-    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
     if out is None:
         out = torch.empty((t_count, heads, KV_LORA_RANK), dtype=torch.bfloat16, device=q.device)
     else:
@@ -264,7 +271,7 @@ def cache_insert(kv_c, k_pe, slot_mapping, kv_cache):
         raise ValueError("slot_mapping must be a contiguous int64 [T] tensor on kv_c's device")
     if not (torch.is_tensor(kv_cache) and kv_cache.device == kv_c.device):
         raise ValueError("kv cache must be on kv_c's device")
-    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
     L = lib()
     with torch.cuda.device(kv_c.device):
         st = L.mla_cache_insert(kv_c.data_ptr(), kv_c.stride(0), k_pe2.data_ptr(), k_pe2.stride(0),
@@ -331,7 +338,7 @@ def decode_q_concat_insert(ql_nope, q_pe, kv_c_normed, k_pe, kv_cache, slot_mapp
             raise ValueError(f"mqa_q must have {b} tokens")
     if not (torch.is_tensor(kv_cache) and kv_cache.device == dev):
         raise ValueError("kv cache must be on ql_nope's device")
-    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
     L = lib()
     with torch.cuda.device(dev):
         st = L.mla_decode_q_concat_insert(
@@ -365,7 +372,7 @@ def gather_upconvert(kv_cache, block_table, cu_seq_lens, num_tokens, *, seq_star
         if kv_cache.ndim != 3:
             raise ValueError("pass block_size for a kv cache that is not [num_blocks, block_size, 656]")
         block_size = kv_cache.shape[1]
-    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
     if not (torch.is_tensor(block_table) and block_table.dtype == torch.int32 and block_table.ndim == 2
             and block_table.device == dev and block_table.stride(1) == 1):
         raise ValueError("block_table must be an int32 [B, W] tensor with contiguous rows on the cache's device")
@@ -449,19 +456,13 @@ def v_up_proj(latent, w_uv, *, gate=None, out=None, prepared=False):
     return out
 
 
-def key_concat_insert(q, k_nope, k_pe, kv_c_normed, kv_cache, slot_mapping, *, positions=None,
-                      cos_sin_cache=None, k_out=None):
-    """MLA prefill epilogue in one launch -> k_out [Tp, H, nope + 64] bf16.
-
-    k_out = [k_nope | k_pe] per head, [kv_c_normed | k_pe] inserted into the
-    fp8_ds_mla cache at slot_mapping (negative = skip); with ``positions`` /
-    ``cos_sin_cache`` GPT-J RoPE is applied to k_pe (in k_out and the
-    record) and to q[..., nope:] in place.  q [Tp, H, nope + 64] (may be
-    None without RoPE), k_nope [Tp, H, nope], k_pe [Tp, 64] or [Tp, 1, 64],
-    kv_c_normed [Tp, 512]; bf16 with a contiguous last dim.
-    """
-    if not (torch.is_tensor(k_nope) and k_nope.is_cuda and k_nope.ndim == 3):
-        raise ValueError("k_nope must be a CUDA bf16 tensor [Tp, H, nope]")
+def _key_concat_args(q, k_nope, k_pe, kv_c_normed, slot_mapping, positions, cos_sin_cache, k_out):
+    """Shape, dtype and device checks of key_concat_insert's tensors, on
+    k_nope's device (any device, so the checks run without a GPU too).
+    Every tensor the kernel reads or writes per token must hold exactly Tp
+    tokens.  Returns (k_pe as [Tp, 64], max_position)."""
+    if not (torch.is_tensor(k_nope) and k_nope.ndim == 3):
+        raise ValueError("k_nope must be a bf16 tensor [Tp, H, nope]")
     dev = k_nope.device
     tp, heads, nope = k_nope.shape
     if not 1 <= heads <= MAX_EPILOGUE_HEADS:
@@ -494,13 +495,35 @@ def key_concat_insert(q, k_nope, k_pe, kv_c_normed, kv_cache, slot_mapping, *, p
                 and cos_sin_cache.device == dev):
             raise ValueError("cos_sin_cache must be a contiguous float32 [max_position, 64] tensor")
         max_position = cos_sin_cache.shape[0]
+    if k_out is not None:
+        _bf16_rows(k_out, "k_out", (heads, nope + QK_ROPE_HEAD_DIM), dev)
+        if k_out.shape[0] != tp:
+            raise ValueError(f"k_out must have {tp} tokens (got {k_out.shape[0]})")
+    return k_pe2, max_position
+
+
+def key_concat_insert(q, k_nope, k_pe, kv_c_normed, kv_cache, slot_mapping, *, positions=None,
+                      cos_sin_cache=None, k_out=None):
+    """MLA prefill epilogue in one launch -> k_out [Tp, H, nope + 64] bf16.
+
+    k_out = [k_nope | k_pe] per head, [kv_c_normed | k_pe] inserted into the
+    fp8_ds_mla cache at slot_mapping (negative = skip); with ``positions`` /
+    ``cos_sin_cache`` GPT-J RoPE is applied to k_pe (in k_out and the
+    record) and to q[..., nope:] in place.  q [Tp, H, nope + 64] (may be
+    None without RoPE), k_nope [Tp, H, nope], k_pe [Tp, 64] or [Tp, 1, 64],
+    kv_c_normed [Tp, 512]; bf16 with a contiguous last dim.
+    """
+    if not (torch.is_tensor(k_nope) and k_nope.is_cuda and k_nope.ndim == 3):
+        raise ValueError("k_nope must be a CUDA bf16 tensor [Tp, H, nope]")
+    dev = k_nope.device
+    tp, heads, nope = k_nope.shape
+    k_pe2, max_position = _key_concat_args(q, k_nope, k_pe, kv_c_normed, slot_mapping, positions,
+                                           cos_sin_cache, k_out)
     if k_out is None:
         k_out = torch.empty((tp, heads, nope + QK_ROPE_HEAD_DIM), dtype=torch.bfloat16, device=dev)
-    else:
-        _bf16_rows(k_out, "k_out", (heads, nope + QK_ROPE_HEAD_DIM), dev)
     if not (torch.is_tensor(kv_cache) and kv_cache.device == dev):
         raise ValueError("kv cache must be on k_nope's device")
-    kv_ptr, n_rec, pitch = _kv_rows(kv_cache)
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
     L = lib()
     with torch.cuda.device(dev):
         st = L.mla_prefill_key_concat_insert(

@@ -105,10 +105,13 @@ typedef enum mla_status {
  *               aligned; used only when the call splits.  A caller-provided
  *               buffer must not be used by another call that may run at the
  *               same time.  NULL: the library uses a buffer it owns per
- *               device (allocated on first need, grown when too small;
- *               growing frees the old buffer with hipFree, which waits for
- *               the device, then calls hipMalloc, so call
- *               mla_workspace_reserve before stream capture).  Every call
+ *               device (allocated with hipMalloc on first need and grown,
+ *               to at least twice its size, when too small; so call
+ *               mla_workspace_reserve before stream capture).  A buffer
+ *               that is replaced stays allocated until the process ends,
+ *               so work queued earlier and graphs captured earlier keep
+ *               valid memory (a graph keeps using the buffer it was
+ *               captured with, not the larger one).  Every call
  *               that passes NULL on a device shares that device's buffer:
  *               two such calls that may overlap (different streams, or
  *               several host threads) race, so give each its own workspace.
@@ -180,8 +183,15 @@ size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int6
                                      uint32_t flags, int device);
 
 /*
- * mla_workspace_reserve - grow the library-owned workspace of `device` to at
- * least `bytes` now (it never shrinks).  Call before stream capture.
+ * mla_workspace_reserve - grow the library-owned split workspace of `device`
+ * to at least `bytes` now (it never shrinks), so that later calls that pass
+ * workspace = NULL allocate nothing; call it before stream capture.  The
+ * library owns this buffer as the decode cores on the kimi_k3
+ * specialized-decode page own theirs (trtllm_decode: one workspace per
+ * device, sized once and reused by every call).  A buffer replaced by a
+ * larger one is kept until the process ends (see mla_sparse_fwd).
+ * Returns MLA_ERR_OUT_OF_MEMORY if the allocation fails, MLA_ERR_HIP if the
+ * device cannot be selected.
  */
 mla_status_t mla_workspace_reserve(int device, size_t bytes);
 
@@ -270,8 +280,8 @@ mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_t
  * [kv_c_normed | RoPE(k_pe)] into the fp8_ds_mla cache.
  *
  * Defined by fused_mla_key_concat_ds_mla_insert (fused_mla_key_concat_kv_cache
- * page: "Concat full K (bf16) and insert the latent in the fp8_ds_mla
- * layout"; q is [Tp, H, qk_head_dim] with RoPE applied in place, k_nope
+ * page: it builds the bf16 full key and writes the latent into the
+ * fp8_ds_mla cache; q is [Tp, H, qk_head_dim] with RoPE applied in place, k_nope
  * [Tp, H, qk_nope_head_dim], k_pe [Tp, 64], the returned key
  * [Tp, H, qk_nope_head_dim + 64]).  RoPE, positions and cos_sin_cache as
  * for mla_decode_q_concat_insert; without them q is left untouched and the

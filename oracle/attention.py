@@ -2,13 +2,14 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The forward is the plain definition of softmax attention, in float64, as the
-flydsl_sparse_mla page describes ``flydsl_sparse_mla_fp8ds_fwd``: row ``t``
-attends ``kv_indices[kv_indptr[t] : kv_indptr[t + 1]]``; negative entries
-are masked; every head of the row uses the same keys (one shared latent KV
-head); ``lse`` is the natural-log log-sum-exp of ``softmax_scale * q.k``
-over the unmasked keys; a row with no unmasked key gives out = 0 and
-lse = -inf.
+The forward is the plain definition of softmax attention, in float64,
+following the ``flydsl_sparse_mla_fp8ds_fwd`` docstring on the
+flydsl_sparse_mla page: the keys of row ``t`` are the slots listed in
+``kv_indices`` between ``kv_indptr[t]`` and ``kv_indptr[t + 1]``, minus the
+negative ones; all heads of a row share those keys (the latent cache has a
+single KV head); the optional LSE is taken in base e over the scaled logits
+of the kept keys; and a row that keeps no key has a zero output with an LSE
+of minus infinity.
 
 Readings where the pages are silent:
 * slot ids >= the number of records are masked like negative ones (the

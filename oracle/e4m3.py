@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The record format on the flydsl_sparse_mla page (module docstring: "512
-e4m3 | 4 f32 per-128 scales | 64 bf16 rope") stores the latent as E4M3,
-and the fused_mla_key_concat_kv_cache page stores it through
-``torch.float8_e4m3fn``.  The ``fp8_word`` helper on the mono/attention/mla
-page names the writer's rounding: vLLM's *saturating* quant.
+The record format in the flydsl_sparse_mla page's module docstring keeps
+the 512 latent values as one E4M3 byte each (next to four float32 tile
+scales and the 64 bf16 rope values), and the fused_mla_key_concat_kv_cache
+page writes them through ``torch.float8_e4m3fn``.  The ``fp8_word`` helper
+on the mono/attention/mla page says the writer's quantization saturates.
 
 Format (OCP 8-bit floating point, E4M3 variant): 1 sign bit, 4 exponent
 bits (bias 7), 3 mantissa bits; exponent field 0 encodes subnormals

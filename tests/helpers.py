@@ -4,12 +4,15 @@ The oracle side never consumes a value produced by the HIP path: its
 records come from the oracle's own writer applied to the generated tokens.
 """
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
-from oracle import encode_records
+from oracle import encode_records, sparse_fwd as oracle_fwd
 from head_latent_attention_sparse_amd.workloads import bf16_bits
 
 # Parity bar for the forward: |out - ref| <= 1e-2 + 1e-2 |ref| elementwise,
@@ -33,6 +36,28 @@ def oracle_encode(kv_c, k_pe):
     return np.concatenate(parts) if parts else np.zeros((0, 656), np.uint8)
 
 
+def oracle_threads():
+    """Threads for oracle work: the CPUs this process may use, at most 16
+    (a GPU machine's CPU share).  numpy releases the GIL in the oracle's array
+    work, so threads share it without extra processes."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _parallel(fn, items):
+    """fn over items on oracle_threads() threads (BLAS pinned to one thread
+    each), results in item order."""
+    with threadpool_limits(limits=1), ThreadPoolExecutor(oracle_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_encode_parallel(kv_c, k_pe):
+    """oracle_encode over CHUNK-token blocks on oracle_threads() threads."""
+    kv_bits, pe_bits = bf16_bits(kv_c), bf16_bits(k_pe.reshape(k_pe.shape[0], -1))
+    parts = _parallel(lambda i: encode_records(kv_bits[i : i + CHUNK], pe_bits[i : i + CHUNK]),
+                      range(0, kv_bits.shape[0], CHUNK))
+    return np.concatenate(parts) if parts else np.zeros((0, 656), np.uint8)
+
+
 def oracle_pool(num_records, batches, fill=0):
     """The whole pool after applying insert batches in order (oracle writer)."""
     pool = np.full((num_records, 656), fill, dtype=np.uint8)
@@ -40,9 +65,20 @@ def oracle_pool(num_records, batches, fill=0):
         slots = b.slots.numpy()
         keep = (slots >= 0) & (slots < num_records)
         if keep.any():
-            rec = oracle_encode(b.kv_c[torch.from_numpy(keep)], b.k_pe[torch.from_numpy(keep)])
+            rec = oracle_encode_parallel(b.kv_c[torch.from_numpy(keep)], b.k_pe[torch.from_numpy(keep)])
             pool[slots[keep]] = rec
     return pool
+
+
+def oracle_fwd_rows(q_bits, pool, indptr, indices, softmax_scale, rows, block=16):
+    """The oracle forward of the listed rows, in blocks of `block` rows run on
+    oracle_threads() threads; returns (out [R, H, 512], lse [R, H]) in row order."""
+    rows = list(rows)
+    blocks = [rows[i : i + block] for i in range(0, len(rows), block)]
+    parts = _parallel(lambda r: oracle_fwd(q_bits, pool, indptr, indices, softmax_scale, rows=r), blocks)
+    if not parts:
+        return np.zeros((0, q_bits.shape[1], 512)), np.zeros((0, q_bits.shape[1]))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
 def oracle_subpool(num_records, batches, slots_needed):

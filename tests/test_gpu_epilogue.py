@@ -144,3 +144,19 @@ def test_prefill_epilogue_strided_and_full():
     check(got_q, got_pool, want_q, want_pool)
     assert np.array_equal(got_k, want_k), "k_out differs"
     assert torch.all(qbuf[:, :, 192:].cpu() == -9.0) and torch.all(kbuf[:, :, 192:].cpu() == -9.0)
+
+
+def test_prefill_epilogue_rejects_k_out_of_another_token_count():
+    """A caller's k_out with fewer (or more) tokens than the inputs is refused
+    before any launch: the pool and the buffers stay untouched."""
+    say("prefill epilogue: k_out with the wrong token count")
+    w = workloads.prefill_epilogue(tokens=6, heads=2, nope=128, pool=64, max_position=64)
+    pool = torch.full((w.num_records, 656), FILL, dtype=torch.uint8, device=DEV)
+    for rows in (5, 7):
+        k_out = torch.full((rows, 2, 192), -3.0, dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(ValueError, match="k_out"):
+            mla.key_concat_insert(w.q.to(DEV), w.k_nope.to(DEV), w.k_pe.to(DEV), w.kv_c.to(DEV), pool,
+                                  w.slots.to(DEV), k_out=k_out)
+        torch.cuda.synchronize()
+        assert torch.all(k_out == -3.0)
+    assert torch.all(pool == FILL)

@@ -17,7 +17,8 @@ import head_latent_attention_sparse_amd as mla
 from head_latent_attention_sparse_amd import workloads
 from head_latent_attention_sparse_amd.workloads import InsertBatch, bf16_bits
 from oracle import decode_records, sparse_fwd as oracle_fwd
-from tests.helpers import (assert_fwd_close, oracle_encode, oracle_subpool, remap_rows, say)
+from tests.helpers import (assert_fwd_close, oracle_encode, oracle_fwd_rows, oracle_pool, oracle_subpool,
+                           oracle_threads, remap_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,15 +90,6 @@ def test_paged_decode_reduced():
     check_rows(w, pool, out, lse, range(8), "paged decode-reduced")
 
 
-def test_paged_decode_full_sampled():
-    say("fwd paged decode full, 6 sampled rows")
-    w = workloads.paged_decode()
-    pool, view = build_gpu_pool(w)
-    out, lse = run_gpu(w, view)
-    check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, [0, 9, 21, 37, 50, 63], "paged decode-full")
-
-
 def test_sparse_prefill_reduced():
     say("fwd sparse prefill reduced (T=96, N=16384)")
     w = workloads.sparse_prefill(tokens=96, records=16384, frac_empty=0.03)
@@ -105,19 +97,6 @@ def test_sparse_prefill_reduced():
     out, lse = run_gpu(w, view)
     check_all_rows_sane(w, out, lse)
     check_rows(w, pool, out, lse, range(96), "sparse prefill-reduced")
-
-
-def test_sparse_prefill_full_sampled():
-    say("fwd sparse prefill full (T=4096, N=131072), sampled rows")
-    w = workloads.sparse_prefill()
-    pool, view = build_gpu_pool(w)
-    out, lse = run_gpu(w, view)
-    check_all_rows_sane(w, out, lse)
-    indptr, ind = w.indptr.numpy(), w.indices.numpy()
-    empty = [t for t in range(w.num_tokens) if np.all(ind[indptr[t]:indptr[t + 1]] < 0)]
-    assert len(empty) == 41
-    rows = sorted(set([0, 1, 777, 2048, 3333, 4095] + empty[:2]))
-    check_rows(w, pool, out, lse, rows, "sparse prefill-full")
 
 
 def test_long_context_reduced():
@@ -129,22 +108,53 @@ def test_long_context_reduced():
     check_rows(w, pool, out, lse, range(3), "long context-reduced")
 
 
-def test_long_context_full_sampled():
-    say("fwd long context full (T=8, N=131072), 2 sampled rows")
+def check_full_workload(w, what):
+    """Every row of a full-size workload against the oracle, in the launch
+    configuration bench.py times (the binding with a caller workspace).  The
+    oracle's pool comes from its own writer applied to the workload's insert
+    batches; the GPU pool (built by mla_cache_insert) must equal it byte for
+    byte first.  Then the properties that hold at any size."""
+    pool, view = build_gpu_pool(w)
+    ref_pool = oracle_pool(w.num_records, w.setup_inserts + w.step_inserts)
+    assert np.array_equal(pool.cpu().numpy(), ref_pool), f"{what}: inserted records differ from the oracle writer"
+    say(f"  {what}: pool bit-exact ({w.num_records} records); GPU forward")
+    need = mla.lib().mla_sparse_fwd_workspace_size(w.num_tokens, w.num_heads, w.nnz, 0, 0)
+    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+    out, lse = run_gpu(w, view, workspace=workspace)
+    check_all_rows_sane(w, out, lse)
+    say(f"  {what}: oracle on all {w.num_tokens} rows ({oracle_threads()} threads)")
+    ref_out, ref_lse = oracle_fwd_rows(bf16_bits(w.q), ref_pool, w.indptr.numpy(), w.indices.numpy(),
+                                       w.softmax_scale, range(w.num_tokens))
+    assert_fwd_close(out, lse, ref_out, ref_lse if lse is not None else None, what)
+    return out, lse
+
+
+def test_paged_decode_full_all_rows():
+    say("fwd paged decode full (B=64): all rows against the oracle")
+    w = workloads.paged_decode()
+    assert mla.split_workgroups(w.num_tokens, w.nnz, torch.cuda.get_device_properties(0).multi_processor_count) > 0
+    check_full_workload(w, "paged decode-full")
+
+
+def test_sparse_prefill_full_all_rows():
+    say("fwd sparse prefill full (T=4096, N=131072): all rows against the oracle")
+    w = workloads.sparse_prefill()
+    indptr, ind = w.indptr.numpy(), w.indices.numpy()
+    empty = [t for t in range(w.num_tokens) if np.all(ind[indptr[t]:indptr[t + 1]] < 0)]
+    assert len(empty) == 41
+    check_full_workload(w, "sparse prefill-full")
+
+
+def test_long_context_full_all_rows():
+    say("fwd long context full (T=8, N=131072): all rows against the oracle")
     w = workloads.long_context()
-    pool, view = build_gpu_pool(w)
-    out, lse = run_gpu(w, view)
-    check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, [0, 5], "long context-full")
+    check_full_workload(w, "long context-full")
 
 
-def test_insert_attend_full_sampled():
-    say("fwd insert + attend full: insert then attend, 12 sampled rows")
+def test_insert_attend_full_all_rows():
+    say("fwd insert + attend full: insert then attend, all rows against the oracle")
     w = workloads.insert_attend()
-    pool, view = build_gpu_pool(w)
-    out, lse = run_gpu(w, view)
-    check_all_rows_sane(w, out, lse)
-    check_rows(w, pool, out, lse, list(range(0, 1024, 93)), "insert + attend-full")
+    check_full_workload(w, "insert + attend-full")
 
 
 # ----------------------------------------------------------------- sweeps and edges

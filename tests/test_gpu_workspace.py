@@ -1,10 +1,14 @@
 """The library-owned split-KV workspace: mla_sparse_fwd called through the C
 ABI with workspace NULL after mla_workspace_reserve of a small size, so the
-library grows its buffer (hipFree of the old one, hipMalloc of the new) on
-the first split call and again for a call that needs more; each result must
-equal, bit for bit, the same call with a caller-provided workspace (the
-binding's path)."""
+library grows its buffer (a new hipMalloc; the old buffer is retired, not
+freed) on the first split call and again for a call that needs more; each
+result must equal, bit for bit, the same call with a caller-provided
+workspace (the binding's path).  A graph captured on the library's buffer
+must still replay correctly after the buffer has been replaced by a larger
+one."""
 
+
+import ctypes
 
 import pytest
 import torch
@@ -32,14 +36,15 @@ def problem(seed, t, heads, n, length):
     return q, pool, ptr.to(DEV), idx.to(DEV)
 
 
-def fwd_library_workspace(q, pool, ptr, idx):
+def fwd_library_workspace(q, pool, ptr, idx, chunk_tiles=0):
     t, heads = q.shape[0], q.shape[1]
     out = torch.empty((t, heads, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((t, heads), dtype=torch.float32, device=DEV)
     L = mla.lib()
     st = L.mla_sparse_fwd(q.data_ptr(), t, heads, q.stride(0), q.stride(1), pool.data_ptr(), pool.shape[0], 656,
                           ptr.data_ptr(), idx.data_ptr(), idx.numel(), SCALE,
-                          ops.FLAG_HAS_INVALID | ops.FLAG_RETURN_LSE, out.data_ptr(), out.stride(0), out.stride(1),
+                          ops.FLAG_HAS_INVALID | ops.FLAG_RETURN_LSE | (chunk_tiles << ops.CHUNK_SHIFT),
+                          out.data_ptr(), out.stride(0), out.stride(1),
                           lse.data_ptr(), None, 0, ops._stream(q.device))
     assert st == 0, L.mla_last_error().decode()
     return out, lse
@@ -61,3 +66,39 @@ def test_library_workspace_grows_and_matches_caller_workspace(order):
         torch.cuda.synchronize()
         assert torch.equal(got_out.view(torch.int16), want_out.view(torch.int16)), f"out differs (H={heads})"
         assert torch.equal(got_lse.view(torch.int32), want_lse.view(torch.int32)), f"lse differs (H={heads})"
+
+
+def test_graph_on_library_workspace_survives_growth():
+    """Capture a NULL-workspace split call in a graph, then make a call that
+    needs a far larger workspace (so the library replaces its buffer) and
+    fill fresh device memory with 0xFF; replaying the graph must still give
+    the eager result bit for bit, since the captured buffer stays allocated."""
+    say("library-owned workspace: graph replay after growth")
+    L = mla.lib()
+    q, pool, ptr, idx = problem(90, 8, 8, 3000, 4000)
+    flags = ops.FLAG_HAS_INVALID | ops.FLAG_RETURN_LSE | (8 << ops.CHUNK_SHIFT)
+    need = L.mla_sparse_fwd_workspace_size(8, 8, idx.numel(), flags, 0)
+    assert 0 < need != ctypes.c_size_t(-1).value
+    assert L.mla_workspace_reserve(0, need) == 0, L.mla_last_error().decode()
+    want_out, want_lse = fwd_library_workspace(q, pool, ptr, idx, chunk_tiles=8)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        got_out, got_lse = fwd_library_workspace(q, pool, ptr, idx, chunk_tiles=8)
+    torch.cuda.synchronize()
+    # 64 rows of 4000 entries in chunks of one tile: ~4064 partials of 16 heads
+    # (about 133 MB), more than any other call in this process needs
+    bq, bpool, bptr, bidx = problem(91, 64, 16, 3000, 4000)
+    big = L.mla_sparse_fwd_workspace_size(64, 16, bidx.numel(), 1 << ops.CHUNK_SHIFT, 0)
+    assert big > 50 * need
+    fwd_library_workspace(bq, bpool, bptr, bidx, chunk_tiles=1)
+    torch.cuda.synchronize()
+    junk = torch.full((4 * need,), 255, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        got_out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got_out.view(torch.int16), want_out.view(torch.int16)), "replay out differs"
+        assert torch.equal(got_lse.view(torch.int32), want_lse.view(torch.int32)), "replay lse differs"
+    del junk
