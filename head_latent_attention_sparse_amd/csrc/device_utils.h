@@ -62,24 +62,6 @@ __device__ __forceinline__ floatx4_t mfma_16x16x32_bf16(bf16x8_t a, bf16x8_t b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// D += A * 2^(ea - 127) . B over K = 128, A and B 32 E4M3 codes per lane
-// (v_mfma_scale_f32_16x16x128_f8f6f4).  Lane (i, g) = (lane % 16, lane / 16)
-// holds row (A) / column (B) i at k = 64 * (byte / 16) + 16 * g + byte % 16;
-// byte OPSEL of lane (i, kb)'s scale word is the e8m0 scale of row i over
-// k-block kb = k / 32.  B is taken unscaled (e8m0 127).
-template <int OPSEL>
-__device__ __forceinline__ floatx4_t mfma_16x16x128_e4m3(intx8_t a, intx8_t b, floatx4_t c, uint32_t scale_a) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, OPSEL, (int)scale_a, 0, 0x7F7F7F7F);
-}
-
-// Two floats -> two E4M3 codes in the low (HI = false) or high 16 bits of
-// `old` (v_cvt_pk_fp8_f32, round to nearest even; used on values that are
-// representable, where it is exact).
-template <bool HI>
-__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

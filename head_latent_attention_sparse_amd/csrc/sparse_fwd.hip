@@ -13,14 +13,12 @@
 //    into registers one tile ahead (4 threads per record), then stored to
 //    LDS as 64 consecutive records; the slot ids of the tile after that are
 //    loaded a tile earlier still;
-//  * QK^T: wave w scores keys 16w..16w+15 of the tile for all 16 head rows.
-//    The latent part runs on the records' E4M3 codes as they are, with the
-//    block-scaled fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): the query is
-//    split once per row into two E4M3 terms with power-of-two block scales
-//    (hi + lo: exact except for elements tiny next to their 32-element
-//    group's max, off by at most 2^-18 of that max), and each key's per-128
-//    tile scale multiplies that tile's float32 partial.  The
-//    rope part is a bf16 MFMA;
+//  * QK^T: wave w scores keys 16w..16w+15 of the tile for all 16 head rows
+//    with bf16 dot products (v_mfma_f32_16x16x32_bf16: exact products,
+//    float32 accumulation).  The records' E4M3 codes are converted to bf16
+//    exactly (every E4M3 value is a bf16 value) and each key's per-128 tile
+//    scale multiplies that tile's float32 partial, so the logits carry no
+//    rounding of code * scale; the rope part is a plain bf16 product;
 //  * the 16x64 logits go through LDS; every wave computes the online-softmax
 //    weights of the whole tile in the exp2 domain (scale * log2 e, as the
 //    FlyDSL launcher passes it) and keeps identical running max / sum; the
@@ -277,19 +275,20 @@ __device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, RowRange &r
   return has_work;
 }
 
-// QK^T partial of latent tile B for this lane's key: sum over the tile's 128
-// dims of (q_hi * 2^-k + q_lo * 2^-(k+k2)) * code, in float32; the key's
-// tile scale is applied by the caller.  Both operands use the MFMA's
-// hardware k order within the tile (k = 64 * (byte / 16) + 16 * g + byte % 16).
+// QK^T partial of latent tile B for this lane's key: the float32 sum over
+// the tile's 128 dims of q * code, four bf16 MFMAs of 32 dims each; the
+// key's tile scale is applied by the caller.  Lane (n, g) holds dims
+// 16g + [0, 16) and 64 + 16g + [0, 16) of the tile, eight per MFMA, in the
+// same order for the query (qa[B][0..3]) and the codes.
 template <int B>
-__device__ __forceinline__ floatx4_t qk_latent_tile(const uint8_t *krec, int g, const intx8_t (&qa)[4][2],
-                                                   const uint32_t (&qscale)[2]) {
+__device__ __forceinline__ floatx4_t qk_latent_tile(const uint8_t *krec, int g, const u32x4_t (&qa)[4][4]) {
   const u32x4_t c0 = *reinterpret_cast<const u32x4_t *>(krec + 128 * B + 16 * g);
   const u32x4_t c1 = *reinterpret_cast<const u32x4_t *>(krec + 128 * B + 64 + 16 * g);
-  const intx8_t codes = {(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
   floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  acc = mfma_16x16x128_e4m3<B>(qa[B][0], codes, acc, qscale[0]);
-  acc = mfma_16x16x128_e4m3<B>(qa[B][1], codes, acc, qscale[1]);
+  acc = mfma_16x16x32_bf16(as_bf16x8(qa[B][0]), e4m3x8_to_bf16x8(c0.x, c0.y), acc);
+  acc = mfma_16x16x32_bf16(as_bf16x8(qa[B][1]), e4m3x8_to_bf16x8(c0.z, c0.w), acc);
+  acc = mfma_16x16x32_bf16(as_bf16x8(qa[B][2]), e4m3x8_to_bf16x8(c1.x, c1.y), acc);
+  acc = mfma_16x16x32_bf16(as_bf16x8(qa[B][3]), e4m3x8_to_bf16x8(c1.z, c1.w), acc);
   return acc;
 }
 
@@ -310,13 +309,14 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // (record, 16-byte sub-chunk) for the gather (see below).
   const int grec = 16 * (tid >> 6) + ((tid >> 4) & 3) + 4 * ((tid >> 2) & 3);
   const int gsub = tid & 3;
-  u32x4_t qr[2];    // query, rope part
-  uint32_t qx[16];  // query, 32 latent values
-  // Query loads are unconditional: a lane past the last head reads the last
-  // head's row and zeroes it.  rope part: bf16 MFMA A operand (row = head
-  // n); lane (n, g) k-slots j of step st <-> rope d = 16g + 8st + j (the
-  // record's rope bytes are read with the same mapping).  latent part: the
-  // 32 values of (head n, latent tile `wave`, k-block g).
+  u32x4_t qr[2];     // query, rope part
+  u32x4_t qa[4][4];  // query, latent part: [tile][MFMA] bf16 A operands
+  // The query is held as bf16 MFMA A operands (row = head n) for the whole
+  // row.  Loads are unconditional: a lane past the last head reads the last
+  // head's row and zeroes it.  rope part: lane (n, g) k-slots j of step st
+  // <-> rope d = 16g + 8st + j; latent tile b, MFMA m: k-slots j <-> dim
+  // 128b + 64(m / 2) + 16g + 8(m % 2) + j.  The records' bytes are read
+  // with the same mappings.
   auto load_query = [&](int64_t t) {
     const int nq = n < p.heads ? n : p.heads - 1;
     const uint32_t qkeep = n < p.heads ? 0xFFFFFFFFu : 0u;
@@ -326,9 +326,14 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + kLatent + 16 * g + 8 * st);
       qr[st] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
     }
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * wave + 32 * g);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) qx[e] = src[e] & qkeep;
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * b + 64 * (m >> 1) + 16 * g + 8 * (m & 1));
+        qa[b][m] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
+      }
+    }
   };
 
   // ---- this workgroup's entries: a whole row, or a chunk of one
@@ -426,9 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // ---- start the first tile early.  The query was requested first, then
   // this thread's slot of tile 0 and the slots of tiles 0 and 1 (for the
   // masks) are taken from the guess or requested now; tile 0's gather is
-  // issued as soon as its slot is in, and the query split is computed while
-  // the gather is in flight.  (The gather is conditional, so anything
-  // loaded after it would wait for it.)
+  // issued as soon as its slot is in.  (The gather is conditional, so
+  // anything loaded after it would wait for it.)
   const bool guessed = guess_beg == rr.beg && rr.vb == 0 && rr.ve == p.guess_len;
   IdxT my_id0, slot_t0, slot_t1;
   if (guessed) {
@@ -441,96 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     slot_t1 = fetch_entry(1, lane);
   }
 
-  // ---- query, latent part: two E4M3 terms per 32-element group, so that
-  // QK^T runs on the records' E4M3 codes directly (scaled fp8 MFMA, no code
-  // conversion).  For the 32 values x of (head h, latent tile blk, k-block
-  // kb), with amax = max |x|:
-  //   y  = x * 2^k,  k = 7 - floor(log2 amax)         (amax * 2^k in [128, 256))
-  //   hi = y with its mantissa cut to 3 bits if |y| >= 2^-6, else 0 (exact E4M3)
-  //   r  = y - hi (exact);  lo = E4M3(r * 2^k2),  k2 = 7 - floor(log2 max |r|)
-  // and x ~ hi * 2^-k + lo * 2^-(k+k2).  Where hi != 0, r holds the 4 bits of
-  // y below hi's, so lo is exact unless r * 2^k2 falls below E4M3's normal
-  // range (error <= 2^-10 * 2^-(k+k2), k2 >= 4: at most 2^-21 of amax).
-  // Where hi = 0 (|y| < 2^-6), r = y keeps bf16's 8 significant bits and lo
-  // rounds it to 4: error <= 2^-4 * 2^-7 * 2^-k, at most 2^-18 of amax
-  // (for amax >= 2^-119, where k is not capped).  The
-  // two powers of two are the e8m0 block scales of the A operand.  Staged through
-  // the tile buffer before its first use: wave w splits latent tile w, lane
-  // (h, kb) = (n, g) one group; then every wave reads all four tiles.
-  intx8_t qa[4][2];     // [latent tile][hi, lo], MFMA A layout
-  uint32_t qscale[2];   // [hi, lo]: byte blk = e8m0 scale of (head n, k-block g) in tile blk
-  {
-    uint8_t *q_lds = s_rec;                     // [(blk * 2 + part) * 16 + h][128] codes
-    uint8_t *sc_lds = s_rec + 4 * 2 * 16 * 128;  // [(part * 16 + h) * 4 + kb] words, byte blk
-    // The query is in by the time the slot of tile 0 is (it was requested
-    // first); it is unpacked before the gather is issued, so the split after
-    // it does not wait for the gather.
-    float x[32];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      x[2 * e] = as_float(qx[e] << 16);
-      x[2 * e + 1] = as_float(qx[e] & 0xFFFF0000u);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    asm volatile("" : : "v"(amax));  // computed here, not sunk past the gather
-    issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0, in flight during the split
-    uint32_t hw[8], lw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hw[i] = lw[i] = 0u;
-    uint32_t e_hi = 127u, e_lo = 127u;
-    if (amax > 0.f) {
-      const int k = min(7 - ((int)(as_u32(amax) >> 23) - 127), 126);
-      const float pk = as_float((uint32_t)(127 + k) << 23);
-      float hv[32];
-      float rmax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float y = x[e] * pk;
-        hv[e] = fabsf(y) >= 0x1p-6f ? as_float(as_u32(y) & 0xFFF00000u) : 0.f;
-        x[e] = y - hv[e];
-        rmax = fmaxf(rmax, fabsf(x[e]));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        hw[i] = pack_e4m3x2<true>(hv[4 * i + 2], hv[4 * i + 3], pack_e4m3x2<false>(hv[4 * i], hv[4 * i + 1], 0u));
-      e_hi = (uint32_t)(127 - k);
-      if (rmax > 0.f) {
-        // k2 >= 0 always (|r| < 256); the cap keeps the lo scale byte >= 1.
-        const int k2 = min(7 - ((int)(as_u32(rmax) >> 23) - 127), 126 - k);
-        const float pk2 = as_float((uint32_t)(127 + k2) << 23);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          lw[i] = pack_e4m3x2<true>(x[4 * i + 2] * pk2, x[4 * i + 3] * pk2,
-                                    pack_e4m3x2<false>(x[4 * i] * pk2, x[4 * i + 1] * pk2, 0u));
-        e_lo = (uint32_t)(127 - k - k2);
-      }
-    }
-    uint8_t *hrow = q_lds + ((wave * 2 + 0) * 16 + n) * 128 + 32 * g;
-    uint8_t *lrow = q_lds + ((wave * 2 + 1) * 16 + n) * 128 + 32 * g;
-    *reinterpret_cast<u32x4_t *>(hrow) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-    *reinterpret_cast<u32x4_t *>(hrow + 16) = u32x4_t{hw[4], hw[5], hw[6], hw[7]};
-    *reinterpret_cast<u32x4_t *>(lrow) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-    *reinterpret_cast<u32x4_t *>(lrow + 16) = u32x4_t{lw[4], lw[5], lw[6], lw[7]};
-    sc_lds[((0 * 16 + n) * 4 + g) * 4 + wave] = (uint8_t)e_hi;
-    sc_lds[((1 * 16 + n) * 4 + g) * 4 + wave] = (uint8_t)e_lo;
-    __syncthreads();
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const uint8_t *row = q_lds + ((blk * 2 + part) * 16 + n) * 128;
-        const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(row + 16 * g);
-        const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(row + 64 + 16 * g);
-        qa[blk][part] = intx8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                                (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      }
-    }
-    qscale[0] = *reinterpret_cast<const uint32_t *>(sc_lds + ((0 * 16 + n) * 4 + g) * 4);
-    qscale[1] = *reinterpret_cast<const uint32_t *>(sc_lds + ((1 * 16 + n) * 4 + g) * 4);
-    __syncthreads();  // the tile buffer is overwritten by the first gather
-  }
+  issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0
 
   float m_run = -INFINITY;  // running max of head n's logits (exp2 domain)
   float l_run = 0.f;        // this lane's part of head n's running sum
@@ -542,10 +457,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     // ---- QK^T for keys 16*wave + n
     const uint8_t *krec = s_rec + (wave * 16 + n) * kRecordBytes;
     const u32x4_t scv = *reinterpret_cast<const u32x4_t *>(krec + kScaleOffset);
-    floatx4_t sacc = qk_latent_tile<0>(krec, g, qa, qscale) * as_float(scv[0]);
-    sacc += qk_latent_tile<1>(krec, g, qa, qscale) * as_float(scv[1]);
-    sacc += qk_latent_tile<2>(krec, g, qa, qscale) * as_float(scv[2]);
-    sacc += qk_latent_tile<3>(krec, g, qa, qscale) * as_float(scv[3]);
+    floatx4_t sacc = qk_latent_tile<0>(krec, g, qa) * as_float(scv[0]);
+    sacc += qk_latent_tile<1>(krec, g, qa) * as_float(scv[1]);
+    sacc += qk_latent_tile<2>(krec, g, qa) * as_float(scv[2]);
+    sacc += qk_latent_tile<3>(krec, g, qa) * as_float(scv[3]);
     {
       const u32x4_t r0 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g);
       const u32x4_t r1 = *reinterpret_cast<const u32x4_t *>(krec + kRopeOffset + 32 * g + 16);
