@@ -116,8 +116,37 @@ int64_t plan_split(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags, int
   return target;
 }
 
+// ---- Fixed split workspace of mla_sparse_fwd_noalloc: a device array of
+// MLA_NOALLOC_SCRATCH_BYTES per GPU, allocated with the code object and held
+// until the process ends.  Host code never names the array in a kernel
+// argument or a copy (the name is only a host-side stand-in): its device
+// address is looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // per device; nullptr until looked up
+
+// Device address of `device`'s scratch array (`device` must be current).
+mla_status_t scratch_address(int device, void **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)device >= g_scratch_ptr.size()) g_scratch_ptr.resize(device + 1, nullptr);
+  if (!g_scratch_ptr[device]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(MLA_ERR_HIP, "mla_sparse_fwd_noalloc: no address for the scratch array on device %d: %s", device,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return MLA_OK;
+}
+
 // The second segment and the sink of mla_sparse_fwd_ex (all absent for mla_sparse_fwd).
 struct FwdExtra {
+  bool scratch = false;  // split workspace from the static scratch array (mla_sparse_fwd_noalloc)
   const float *sink = nullptr;
   const void *records = nullptr;
   int64_t num_records = 0, record_stride = MLA_RECORD_BYTES;
@@ -236,7 +265,14 @@ mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_head
   if (bound > 0) {
     const mla::SplitLayout l = mla::split_layout(num_tokens, num_heads, bound);
     void *ws = workspace;
-    if (ws) {
+    if (x.scratch) {
+      if (l.bytes > kScratchBytes)
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "mla_sparse_fwd_noalloc: this call needs %zu bytes of split workspace, the fixed scratch holds %zu",
+                    l.bytes, kScratchBytes);
+      mla_status_t st = scratch_address(device, &ws);
+      if (st != MLA_OK) return st;
+    } else if (ws) {
       if (workspace_bytes < l.bytes)
         return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace of %zu bytes, %zu needed", workspace_bytes, l.bytes);
       if (!aligned(ws, 256)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: workspace not 256-byte aligned");
@@ -289,6 +325,17 @@ mla_status_t mla_sparse_fwd_ex(const void *q, int64_t num_tokens, int32_t num_he
                          out_stride_token, out_stride_head, lse, workspace, workspace_bytes, stream, x);
 }
 
+mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                                    int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                                    int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                                    int64_t num_indices, float softmax_scale, uint32_t flags, void *out,
+                                    int64_t out_stride_token, int64_t out_stride_head, float *lse, void *stream) {
+  FwdExtra x;
+  x.scratch = true;
+  return sparse_fwd_impl(q, num_tokens, num_heads, q_stride_token, q_stride_head, kv_records, num_records,
+                         record_stride, kv_indptr, kv_indices, num_indices, softmax_scale, flags, out,
+                         out_stride_token, out_stride_head, lse, nullptr, 0, stream, x);
+}
 
 const char *mla_last_error(void) { return g_error; }
 

@@ -43,6 +43,8 @@ SIGNATURES = {
                               _P, _P, _SZ, _P]),
     "mla_sparse_fwd_ex": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _P, _P, _I64, _I64, _P, _P,
                                  _I64, _F32, _U32, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "mla_sparse_fwd_noalloc": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P, _I64,
+                                      _I64, _P, _P]),
     "mla_sparse_fwd_split_workgroups": (_I64, [_I64, _I64, _I32, _U32]),
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),

@@ -160,6 +160,27 @@ mla_status_t mla_sparse_fwd_ex(const void *q, int64_t num_tokens, int32_t num_he
                                float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mla_sparse_fwd_noalloc - mla_sparse_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  It takes no workspace and allocates
+ * nothing (no hipMalloc, hipFree or allocating library call): a call that
+ * splits keeps its partials in a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its load
+ * until the process ends.  A call whose split workspace
+ * (mla_sparse_fwd_workspace_size) is larger returns MLA_ERR_UNSUPPORTED and
+ * queues nothing.  All calls on one GPU share that array, which keeps the
+ * last call's contents: two calls that may overlap on one GPU (different
+ * streams or host threads) race.  Arguments as for mla_sparse_fwd without
+ * workspace / workspace_bytes; results equal mla_sparse_fwd's bit for bit.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                                    int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                                    int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                                    int64_t num_indices, float softmax_scale, uint32_t flags, void *out,
+                                    int64_t out_stride_token, int64_t out_stride_head, float *lse, void *stream);
+
+/*
  * mla_sparse_fwd_split_workgroups - the split-KV plan mla_sparse_fwd uses
  * (host only, no device access): 0 = one workgroup per row; otherwise the
  * number of workgroups of the partial pass, an upper bound on the number of
@@ -405,7 +426,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 8
+#define MLA_ABI_VERSION 9
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus
