@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FWD_KERNEL_SOURCE = os.path.join(ROOT, "head_latent_attention_sparse_amd", "csrc", "sparse_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_fwd_sparse_prefill_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "sparse_fwd_sparse_prefill_mfma.json")
 
 WORKLOAD_NAMES = {
     1: "tiny: T=4 rows, H=16, 128 distinct slots/row over 2048 records",
@@ -53,7 +54,10 @@ def parse():
                     help="workload: 1 tiny, 2 paged decode, 3 sparse top-k prefill, 4 long context, "
                          "5 insert + attend")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes for cpu_baseline (default: the usable cores, at most 16)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only the --config workload (default: the other four are timed too)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration under rocprofv3 --pmc)")
     ap.add_argument("--epilogue", action="store_true",
@@ -100,47 +104,58 @@ def main():
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
               "(rows would shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
+    modes = {"epilogue": "bench_epilogue", "prefill_epilogue": "bench_prefill_epilogue", "gather": "bench_gather",
+             "vproj": "bench_vproj", "decode_step": "bench_decode_step", "insert": "bench_insert"}
+    for flag, fn in modes.items():
+        if getattr(args, flag):
+            import torch
 
+            dev = torch.device("cuda:0")
+            torch.cuda.set_device(dev)
+            globals()[fn](args, dev)
+            return
+    bench_forward(args)
+
+
+def input_hash(w, seg=None):
+    """SHA-256 of every input of a forward workload as the GPU receives it:
+    query, CSR, the insert batches that build (and, for insert + attend,
+    update) the pool, the softmax scale and flags, and the sink and second
+    segment when given."""
+    import numpy as np
+    import torch
+
+    h = hashlib.sha256()
+    parts = [w.q, w.indptr, w.indices]
+    for b in w.setup_inserts + w.step_inserts:
+        parts += [b.kv_c, b.k_pe, b.slots]
+    if seg is not None:
+        parts += [seg.sink, seg.indptr, seg.indices, seg.insert.kv_c, seg.insert.k_pe, seg.insert.slots]
+    for x in parts:
+        h.update(x.contiguous().view(-1).view(torch.uint8).numpy().tobytes())
+    h.update(np.float32(w.softmax_scale).tobytes())
+    h.update(bytes([int(w.has_invalid), int(w.return_lse), w.num_heads, w.block_size or 0]))
+    return h.hexdigest()
+
+
+def measure_forward(w, args, dev, seg=None):
+    """Resident inputs, W warmup steps, then K timed steps of the workload's
+    hot path (the step's inserts, then mla_sparse_fwd), a HIP event pair per
+    step on the launch stream.  Returns the timings and sizes."""
     import numpy as np
     import torch
 
     import head_latent_attention_sparse_amd as mla
-    from head_latent_attention_sparse_amd import workloads
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.epilogue:
-        bench_epilogue(args, dev)
-        return
-    if args.prefill_epilogue:
-        bench_prefill_epilogue(args, dev)
-        return
-    if args.gather:
-        bench_gather(args, dev)
-        return
-    if args.vproj:
-        bench_vproj(args, dev)
-        return
-    if args.decode_step:
-        bench_decode_step(args, dev)
-        return
-    if args.insert:
-        bench_insert(args, dev)
-        return
-    log(f"generating workload {args.config}")
-    w = workloads.WORKLOADS[args.config]()
     t_count, heads = w.num_tokens, w.num_heads
     nnz, nnz_valid = w.nnz, w.nnz_valid()
-
-    # ---- inputs resident in HBM
     pool = torch.zeros((w.num_records, 656), dtype=torch.uint8, device=dev)
     view = pool.view(-1, w.block_size, 656) if w.block_size else pool
     for b in w.setup_inserts:
         mla.cache_insert(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev), view)
     step_inserts = [(b.kv_c.to(dev), b.k_pe.to(dev), b.slots.to(dev)) for b in w.step_inserts]
     ex = {}
-    if args.with_sink_extra:
-        seg = workloads.extra_segment(t_count, heads)
+    if seg is not None:
         pool2 = torch.zeros((seg.num_records, 656), dtype=torch.uint8, device=dev)
         mla.cache_insert(seg.insert.kv_c.to(dev), seg.insert.k_pe.to(dev), seg.insert.slots.to(dev), pool2)
         ex = dict(attn_sink=seg.sink.to(dev), extra_kv=pool2, extra_indptr=seg.indptr.to(dev),
@@ -152,7 +167,7 @@ def main():
     out = torch.empty((t_count, heads, 512), dtype=torch.bfloat16, device=dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     split_wgs = mla.split_workgroups(t_count, nnz, cus)
-    ws_bytes = mla.lib().mla_sparse_fwd_workspace_size(t_count, heads, nnz, 0, 0)
+    ws_bytes = mla.lib().mla_sparse_fwd_workspace_size(t_count, heads, nnz, 0, dev.index or 0)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -170,13 +185,11 @@ def main():
         return mla.sparse_fwd(q, view, indptr, indices, w.softmax_scale, has_invalid=w.has_invalid,
                               out=out, return_lse=w.return_lse, workspace=workspace, **ex)
 
-    log("inputs resident; warmup")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    # ---- timed region: K steps; a HIP event pair around each step on the
-    # stream the kernels are launched on (torch's current stream).
+    # timed region: K steps; a HIP event pair around each step on the stream
+    # the kernels are launched on (torch's current stream)
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -187,70 +200,134 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
-    dev_ms = float(np.mean(step_ms))
-
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     _, lse = step()
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all(), "non-finite output"
 
-    pairs_h = nnz * heads
-    value = pairs_h / (ms_per_step * 1e-3)
-    gathered = nnz_valid * 656.0
-    # every byte the call must move once: records gathered, the query, the CSR
-    # lists, out and lse (plus the second list and the sinks when given)
-    total_bytes = (gathered + q.numel() * 2 + indptr.numel() * indptr.element_size()
+    total_bytes = (nnz_valid * 656.0 + q.numel() * 2 + indptr.numel() * indptr.element_size()
                    + indices.numel() * indices.element_size() + out.numel() * 2
                    + (t_count * heads * 4 if w.return_lse else 0))
     if ex:
         total_bytes += (ex["extra_indptr"].numel() * ex["extra_indptr"].element_size()
                         + ex["extra_indices"].numel() * ex["extra_indices"].element_size() + heads * 4)
-    # inserts inside the step: [kv_c | k_pe] and the slot read, a record written
-    for kv_c, k_pe, slots in step_inserts:
+    for kv_c, k_pe, slots in step_inserts:  # [kv_c | k_pe] and the slot read, a record written
         total_bytes += kv_c.numel() * 2 + k_pe.numel() * 2 + slots.numel() * 8 + int((slots >= 0).sum()) * 656
-    flops = nnz_valid * heads * 2.0 * (576 + 512)
-    achieved_gbps = gathered / (dev_ms * 1e-3) / 1e9
+    return dict(nnz=nnz, nnz_valid=nnz_valid, heads=heads, tokens=t_count, split_wgs=split_wgs,
+                ms_per_step=wall * 1e3 / args.steps, dev_ms_mean=float(step_ms.mean()),
+                dev_ms_median=float(np.median(step_ms)), total_bytes=total_bytes)
 
+
+def config_summary(k, w, r, seg=None):
+    """Per-workload figures for the JSON line."""
+    gathered = r["nnz_valid"] * 656.0
+    gbps = gathered / (r["dev_ms_mean"] * 1e-3) / 1e9
+    return {
+        "workload": WORKLOAD_NAMES[k],
+        "rows": r["tokens"],
+        "heads": r["heads"],
+        "csr_entries": r["nnz"],
+        "valid_entries": r["nnz_valid"],
+        "split_kv_workgroups": r["split_wgs"],
+        "device_us_mean": r["dev_ms_mean"] * 1e3,
+        "device_us_median": r["dev_ms_median"] * 1e3,
+        "pairs_H_per_s": r["nnz"] * r["heads"] / (r["ms_per_step"] * 1e-3),
+        "record_GBps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "mfma_tflops": r["nnz_valid"] * r["heads"] * 2.0 * (576 + 512) / (r["dev_ms_mean"] * 1e-3) / 1e12,
+        "input_sha256": input_hash(w, seg),
+    }
+
+
+def bench_forward(args):
+    """The forward workloads: the headline one (--config, default the sparse
+    top-k prefill) gives metric / value / roofline; the other four are timed
+    the same way and reported under "configs"; the fp64 oracle is timed on
+    the headline workload's rows on the host's cores."""
+    import torch
+
+    from head_latent_attention_sparse_amd import workloads
+
+    log(f"generating workload {args.config}")
+    w = workloads.WORKLOADS[args.config]()
+    seg = workloads.extra_segment(w.num_tokens, w.num_heads) if args.with_sink_extra else None
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's records and worker processes are set up before anything touches the GPU
+        cpu = CpuOracle(w, seg, args.cpu_workers)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("headline workload: inputs resident; warmup and timed steps")
+    r = measure_forward(w, args, dev, seg)
+    head = config_summary(args.config, w, r, seg)
+    log(f"timed {args.steps} steps: {r['ms_per_step']:.3f} ms/step (device mean {r['dev_ms_mean']:.3f} ms, "
+        f"median {r['dev_ms_median']:.3f} ms)")
+    configs = {}
+    if not args.no_other_configs and seg is None:
+        for k in sorted(WORKLOAD_NAMES):
+            if k == args.config:
+                continue
+            log(f"workload {k}")
+            wk = workloads.WORKLOADS[k]()
+            configs[str(k)] = config_summary(k, wk, measure_forward(wk, args, dev))
+            del wk
+            torch.cuda.empty_cache()
+
+    gathered = r["nnz_valid"] * 656.0
+    dev_ms = r["dev_ms_mean"]
+    achieved_gbps = gathered / (dev_ms * 1e-3) / 1e9
+    flops = r["nnz_valid"] * r["heads"] * 2.0 * (576 + 512)
     traffic = None
-    if os.path.exists(TRAFFIC_FILE) and args.config == 3 and not args.with_sink_extra:
+    if os.path.exists(TRAFFIC_FILE) and args.config == 3 and seg is None:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha256_16") == source_hash():
             traffic = tr.get("bytes_per_launch")
+    mfma = None
+    if os.path.exists(MFMA_FILE) and args.config == 3 and seg is None:
+        with open(MFMA_FILE) as f:
+            mf = json.load(f)
+        if mf.get("kernel_source_sha256_16") == source_hash():
+            mfma = mf.get("mfma_busy_frac")
 
     result = {
         "metric": "sparse MLA fwd: (row,key) pairs/s x H and achieved HBM GB/s on 656B records",
-        "value": value,
+        "value": r["nnz"] * r["heads"] / (r["ms_per_step"] * 1e-3),
         "unit": "pairs*H/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "arithmetic": "bf16 MFMA dot products with float32 accumulation for QK^T and PV (E4M3 record codes "
+                      "converted exactly to bf16, per-128 tile scales applied in float32), float32 softmax",
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.config] + (
                 "; + per-head sink and a second segment of 256 slots/row over 16384 more records"
-                if args.with_sink_extra else ""),
-            "rows": t_count,
-            "heads": heads,
+                if seg is not None else ""),
+            "rows": r["tokens"],
+            "heads": r["heads"],
             "records": w.num_records,
-            "csr_entries": nnz,
-            "valid_entries": nnz_valid,
-            "split_kv_workgroups": split_wgs,
+            "csr_entries": r["nnz"],
+            "valid_entries": r["nnz_valid"],
+            "split_kv_workgroups": r["split_wgs"],
+            "input_sha256": head["input_sha256"],
             "parallelism": "single GPU",
         },
-        "gathered_record_GBps": gathered / (ms_per_step * 1e-3) / 1e9,
-        "total_algorithmic_bytes": total_bytes,
-        "total_algorithmic_GBps": total_bytes / (dev_ms * 1e-3) / 1e9,
-        "valid_pairs_H_per_s": nnz_valid * heads / (ms_per_step * 1e-3),
+        "gathered_record_GBps": gathered / (r["ms_per_step"] * 1e-3) / 1e9,
+        "total_algorithmic_bytes": r["total_bytes"],
+        "total_algorithmic_GBps": r["total_bytes"] / (dev_ms * 1e-3) / 1e9,
+        "valid_pairs_H_per_s": r["nnz_valid"] * r["heads"] / (r["ms_per_step"] * 1e-3),
         "device_ms_per_step": dev_ms,
+        "device_ms_per_step_median": r["dev_ms_median"],
         "mfma_tflops": flops / (dev_ms * 1e-3) / 1e12,
-        "mfma_frac": flops / (dev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mfma_frac_algorithmic": flops / (dev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mfma_busy_frac": mfma,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved_gbps,
@@ -260,12 +337,12 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": gathered,
         },
+        "configs": configs,
     }
-
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {dev_ms:.3f} ms)")
-    if not args.no_cpu_baseline:
+    if cpu is not None:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, seg if args.with_sink_extra else None)
+        result["cpu_baseline"] = cpu.run()
+        cpu.close()
     print(json.dumps(result), flush=True)
 
 
@@ -714,54 +791,78 @@ def bench_decode_step(args, dev):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, target_seconds, seg=None):
-    """The fp64 oracle on a bounded sample of the same workload's rows (with
-    the sink and second segment when `seg` is given)."""
-    import numpy as np
+# ---- the oracle on the host's cores.  The worker processes are forked
+# from this process before it touches the GPU; they inherit the oracle's
+# records and the workload (copy on write) and run numpy only.
+_CPU = {}
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
 
-    from oracle import encode_records, sparse_fwd
-    from head_latent_attention_sparse_amd.workloads import bf16_bits
+    _CPU["limits"] = threadpool_limits(limits=1)  # one BLAS thread per process
 
-    indptr, indices = w.indptr.numpy().astype(np.int64), w.indices.numpy().astype(np.int64)
-    batches = w.setup_inserts + w.step_inserts
-    with threadpool_limits(limits=1):
-        # records of the workload, by the oracle's own writer (untimed setup)
+
+def _cpu_worker_rows(rows):
+    from oracle import sparse_fwd
+
+    sparse_fwd(_CPU["q_bits"], _CPU["pool"], _CPU["indptr"], _CPU["indices"], _CPU["scale"], rows=rows,
+               extra=_CPU["extra"], sink=_CPU["sink"])
+    return len(rows)
+
+
+class CpuOracle:
+    """The fp64 numpy oracle forward over all rows of a workload, in blocks of
+    rows on a pool of worker processes (one per core the process may use, at
+    most 16: a GPU machine's CPU share)."""
+
+    def __init__(self, w, seg=None, workers=0):
+        import multiprocessing
+
+        import numpy as np
+
+        from oracle import encode_records
+        from head_latent_attention_sparse_amd.workloads import bf16_bits
+
+        log("cpu baseline: the oracle's own records (untimed)")
         pool = np.zeros((w.num_records, 656), dtype=np.uint8)
-        for b in batches:
+        for b in w.setup_inserts + w.step_inserts:
             slots = b.slots.numpy()
             keep = (slots >= 0) & (slots < w.num_records)
             kv, pe = bf16_bits(b.kv_c)[keep], bf16_bits(b.k_pe)[keep]
             recs = [encode_records(kv[i:i + 8192], pe[i:i + 8192]) for i in range(0, kv.shape[0], 8192)]
             pool[slots[keep]] = np.concatenate(recs)
-        q_bits = bf16_bits(w.q)
-        extra, sink, eptr = None, None, None
+        _CPU.update(q_bits=bf16_bits(w.q), pool=pool, indptr=w.indptr.numpy().astype(np.int64),
+                    indices=w.indices.numpy().astype(np.int64), scale=w.softmax_scale, extra=None, sink=None)
+        self.pairs = int(w.nnz)
         if seg is not None:
-            eptr = seg.indptr.numpy().astype(np.int64)
             pool2 = encode_records(bf16_bits(seg.insert.kv_c), bf16_bits(seg.insert.k_pe))  # slots 0..N2-1 in order
-            extra = (pool2, eptr, seg.indices.numpy().astype(np.int64))
-            sink = seg.sink.numpy()
-        log("oracle records written; timing the oracle forward")
-        rows, pairs, elapsed, t = [], 0, 0.0, 0
-        # rows in order until the target CPU time is reached
-        while t < w.num_tokens and elapsed < target_seconds:
-            batch = list(range(t, min(t + 8, w.num_tokens)))
-            t0 = time.perf_counter()
-            sparse_fwd(q_bits, pool, indptr, indices, w.softmax_scale, rows=batch, extra=extra, sink=sink)
-            elapsed += time.perf_counter() - t0
-            pairs += int(indptr[batch[-1] + 1] - indptr[batch[0]])
-            if eptr is not None:
-                pairs += int(eptr[batch[-1] + 1] - eptr[batch[0]])
-            rows.extend(batch)
-            t += len(batch)
-    return {
-        "value": pairs * w.num_heads / elapsed,
-        "unit": "pairs*H/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"rows 0..{len(rows) - 1} of {w.num_tokens} ({pairs} CSR entries), fp64 numpy oracle, "
-                  f"one thread, {elapsed:.1f} s",
-    }
+            _CPU.update(extra=(pool2, seg.indptr.numpy().astype(np.int64), seg.indices.numpy().astype(np.int64)),
+                        sink=seg.sink.numpy())
+            self.pairs += int(seg.indices.numel())
+        self.rows, self.heads = w.num_tokens, w.num_heads
+        self.workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+        self.procs = multiprocessing.get_context("fork").Pool(self.workers, initializer=_cpu_worker_init)
+
+    def run(self):
+        blocks = [list(range(i, min(i + 8, self.rows))) for i in range(0, self.rows, 8)]
+        self.procs.map(_cpu_worker_rows, blocks[: self.workers])  # first touch of the pages in every worker
+        t0 = time.perf_counter()
+        done = sum(self.procs.map(_cpu_worker_rows, blocks, chunksize=1))
+        elapsed = time.perf_counter() - t0
+        assert done == self.rows
+        return {
+            "value": self.pairs * self.heads / elapsed,
+            "unit": "pairs*H/s",
+            "cores": self.workers,
+            "kind": "oracle",
+            "sample": f"all {self.rows} rows ({self.pairs} CSR entries) of the same workload, fp64 numpy oracle, "
+                      f"{self.workers} worker processes with one BLAS thread each, {elapsed:.2f} s wall",
+        }
+
+    def close(self):
+        self.procs.close()
+        self.procs.join()
 
 
 if __name__ == "__main__":

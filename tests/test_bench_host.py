@@ -43,3 +43,34 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_input_hash_is_stable_and_sees_every_input():
+    from head_latent_attention_sparse_amd import workloads
+
+    w = workloads.tiny()
+    h = bench.input_hash(w)
+    assert h == bench.input_hash(workloads.tiny()) and len(h) == 64
+    w.indices[5] = -1
+    assert bench.input_hash(w) != h
+    w = workloads.tiny()
+    w.setup_inserts[0].kv_c[3, 7] = 2.0
+    assert bench.input_hash(w) != h
+    w = workloads.tiny()
+    w.softmax_scale *= 2
+    assert bench.input_hash(w) != h
+
+
+def test_cpu_oracle_pool_runs_every_row():
+    """The baseline's worker pool (forked, numpy only) covers every row once and
+    reports the worker count as its cores."""
+    from head_latent_attention_sparse_amd import workloads
+
+    w = workloads.tiny()
+    cpu = bench.CpuOracle(w, workers=2)
+    try:
+        r = cpu.run()
+    finally:
+        cpu.close()
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert f"all {w.num_tokens} rows" in r["sample"]
