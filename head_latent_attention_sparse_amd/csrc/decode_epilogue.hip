@@ -22,8 +22,9 @@
 // each product and the sum rounded to float32 (no fused multiply-add), then
 // to bf16 round-to-nearest-even.
 //
-// One workgroup per token: wave 0 writes the record (write_record_wave),
-// then all four waves copy the query, 16 bytes per thread per step.
+// One workgroup per token: wave 0 loads the record's inputs, every thread
+// loads its first batch of query (or key) chunks, then wave 0 writes the
+// record and every thread its chunks, 16 bytes per thread per chunk.
 #include "mla_internal.h"
 #include "record_writer.h"
 
@@ -32,7 +33,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunksPerHead = kQkDim / 8;  // 72 x 8 bf16
-constexpr int kBatch = 8;                   // chunks in flight per thread
+// chunks whose loads a thread keeps in flight together
+constexpr int kBatchDecode = 4;
+constexpr int kBatchPrefill = 2;
 
 #pragma clang fp contract(off)
 // GPT-J rotation of one pair, float32 with a rounding after every operation.
@@ -48,6 +51,34 @@ __device__ __forceinline__ uint32_t rope_word(uint32_t w, float c, float s) {
   return pack_bf16x2(y0, y1);
 }
 
+// The record's inputs, loaded by wave 0 (tid < 64) of the token's workgroup.
+struct RecordLoads {
+  int64_t slot;
+  u32x4_t latent;
+  uint32_t pe;  // rope word tid (tid < 32), before RoPE
+};
+
+__device__ __forceinline__ RecordLoads load_record_inputs(int tid, int64_t b, const int64_t *slots, const uint16_t *kv_c,
+                                                          int64_t kv_c_stride, const uint16_t *k_pe, int64_t k_pe_stride) {
+  RecordLoads r{-1, u32x4_t{0u, 0u, 0u, 0u}, 0u};
+  if (tid < 64) {
+    r.slot = slots[b];
+    r.latent = load_latent_lane(tid, kv_c + b * kv_c_stride);
+    if (tid < 32) r.pe = reinterpret_cast<const uint32_t *>(k_pe + b * k_pe_stride)[tid];
+  }
+  return r;
+}
+
+// Wave 0 rotates the rope words (when cs is set) and writes the record,
+// unless the slot is -1 or out of range.
+__device__ __forceinline__ void store_record(int tid, const RecordLoads &r, const float *cs, int64_t num_records,
+                                             uint8_t *records) {
+  if (tid >= 64 || r.slot < 0 || r.slot >= num_records) return;
+  uint32_t w = r.pe;
+  if (cs && tid < 32) w = rope_word(w, cs[tid], cs[32 + tid]);
+  encode_store_record(tid, r.latent, w, records + r.slot * kRecordBytes);
+}
+
 __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogueArgs a) {
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -58,27 +89,20 @@ __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogu
     cs = a.cos_sin + pos * kRope;
   }
 
-  // ---- the record (wave 0)
-  if (tid < 64) {
-    const int64_t slot = a.slots[b];
-    if (slot >= 0 && slot < a.num_records) {
-      const int lane = tid;
-      const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
-      uint32_t w = lane < 32 ? pe[lane] : 0u;
-      if (cs && lane < 32) w = rope_word(w, cs[lane], cs[32 + lane]);
-      write_record_wave(lane, a.kv_c + b * a.kv_c_stride, w, a.records + slot * kRecordBytes);
-    }
-  }
+  // ---- the record's loads (wave 0), issued before the query's so that no
+  // load waits on a store; the record is encoded after the first batch.
+  RecordLoads rl = load_record_inputs(tid, b, a.slots, a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride);
+  bool record_pending = true;
 
   // ---- the query: chunk j of head h holds columns 8j .. 8j+7 of the 576.
-  // Batches of kBatch chunks per thread: all loads first, then the stores
+  // Batches of kBatchDecode chunks per thread: all loads first, then the stores
   // (the output may alias the inputs as far as the compiler knows, so loads
   // after a store would wait for it).
   const int chunks = a.num_heads * kChunksPerHead;
-  for (int base = 0; base < chunks; base += kThreads * kBatch) {
-    u32x4_t w[kBatch];
+  for (int base = 0; base < chunks; base += kThreads * kBatchDecode) {
+    u32x4_t w[kBatchDecode];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatchDecode; ++k) {
       const int c = base + tid + kThreads * k;
       if (c >= chunks) break;
       const int h = c / kChunksPerHead;
@@ -90,8 +114,12 @@ __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogu
                                                                      (int64_t)h * a.qpe_stride_head + 8 * (j - kLatent / 8));
       w[k] = u32x4_t{src[0], src[1], src[2], src[3]};
     }
+    if (record_pending) {
+      record_pending = false;
+      store_record(tid, rl, cs, a.num_records, a.records);
+    }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatchDecode; ++k) {
       const int c = base + tid + kThreads * k;
       if (c >= chunks) break;
       const int h = c / kChunksPerHead;
@@ -107,6 +135,7 @@ __global__ __launch_bounds__(kThreads) void decode_epilogue_kernel(DecodeEpilogu
       for (int i = 0; i < 4; ++i) dst[i] = w[k][i];
     }
   }
+  if (record_pending) store_record(tid, rl, cs, a.num_records, a.records);
 }
 
 __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilogueArgs a) {
@@ -119,17 +148,9 @@ __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilo
     cs = a.cos_sin + pos * kRope;
   }
 
-  // ---- the record (wave 0)
-  if (tid < 64) {
-    const int64_t slot = a.slots[b];
-    if (slot >= 0 && slot < a.num_records) {
-      const int lane = tid;
-      const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
-      uint32_t w = lane < 32 ? pe[lane] : 0u;
-      if (cs && lane < 32) w = rope_word(w, cs[lane], cs[32 + lane]);
-      write_record_wave(lane, a.kv_c + b * a.kv_c_stride, w, a.records + slot * kRecordBytes);
-    }
-  }
+  // ---- the record's loads (wave 0) first; encoded after the first batch
+  RecordLoads rl = load_record_inputs(tid, b, a.slots, a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride);
+  bool record_pending = true;
 
   // ---- k_out = [k_nope | RoPE(k_pe)] and, with RoPE, q's rope part in
   // place: per head, nope / 8 key chunks from k_nope, 8 rotated k_pe chunks
@@ -139,12 +160,12 @@ __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilo
   const int chunks = a.num_heads * per_head;
   const uint32_t *pe = reinterpret_cast<const uint32_t *>(a.k_pe + b * a.k_pe_stride);
   // kind of chunk j of a head: 0 = k_nope -> k_out, 1 = RoPE(k_pe) -> k_out,
-  // 2 = q's rope part in place.  Batches of kBatch chunks per thread: all
+  // 2 = q's rope part in place.  Batches of kBatchPrefill chunks per thread: all
   // loads first, then the stores (see the decode kernel).
-  for (int base = 0; base < chunks; base += kThreads * kBatch) {
-    u32x4_t w[kBatch];
+  for (int base = 0; base < chunks; base += kThreads * kBatchPrefill) {
+    u32x4_t w[kBatchPrefill];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatchPrefill; ++k) {
       const int c = base + tid + kThreads * k;
       if (c >= chunks) break;
       const int h = c / per_head;
@@ -159,8 +180,12 @@ __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilo
                                                  8 * (j - nk - 8));
       w[k] = u32x4_t{src[0], src[1], src[2], src[3]};
     }
+    if (record_pending) {
+      record_pending = false;
+      store_record(tid, rl, cs, a.num_records, a.records);
+    }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < kBatchPrefill; ++k) {
       const int c = base + tid + kThreads * k;
       if (c >= chunks) break;
       const int h = c / per_head;
@@ -183,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void prefill_epilogue_kernel(PrefillEpilo
       for (int i = 0; i < 4; ++i) dst[i] = w[k][i];
     }
   }
+  if (record_pending) store_record(tid, rl, cs, a.num_records, a.records);
 }
 
 }  // namespace

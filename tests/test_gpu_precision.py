@@ -200,6 +200,37 @@ def test_encoder_every_bf16_value_at_scale_one():
     assert np.all(scales.reshape(-1)[:real] == 1.0)
 
 
+def test_encoder_every_bf16_value_under_chosen_tile_maxima():
+    """For a set of tile maxima, every bf16 value of magnitude at most that
+    maximum (both signs, zeros and subnormals included) in tiles led by the
+    maximum.  The maxima: the smallest subnormals and the smallest normal,
+    two neighbours on either side of 0x15DF / 0x15E0 (about 1.75 * 2^-84),
+    where the scale max / 448 crosses 2^-92 and the writer switches from
+    dividing to multiplying by the rounded reciprocal with one correction
+    step, the same around 2^-125 (0x055F / 0x0560), all-ones and zero
+    mantissas across the exponent range, and random ones.  Each code must
+    equal the oracle's, whose quotient is numpy's IEEE float32 division."""
+    say("encoder: every bf16 value under chosen tile maxima")
+    rng = np.random.default_rng(47)
+    tops = [0x0001, 0x0002, 0x007F, 0x0080, 0x055E, 0x055F, 0x0560, 0x0561, 0x15DE, 0x15DF, 0x15E0, 0x15E1]
+    for e in (-120, -64, -20, -7, -1, 0, 1, 3, 8, 9, 20, 64, 127):
+        tops += [((e + 127) << 7) | 0x7F, ((e + 127) << 7), ((e + 127) << 7) | int(rng.integers(1, 0x7F))]
+    tops = [t for t in tops if t <= 0x7F7F]  # finite
+    tops += [int(t) for t in rng.integers(0x0080, 0x7F7F, 8)]
+    tiles = []
+    for t in tops:
+        mags = np.arange(0, t + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | 0x8000])
+        vals = vals[rng.permutation(vals.size)]
+        n = -(-vals.size // 127)
+        vals = np.concatenate([vals, np.zeros(n * 127 - vals.size, np.uint16)]).reshape(n, 127)
+        lead = np.where(rng.random(n) < 0.5, t, t | 0x8000).astype(np.uint16)[:, None]
+        tiles.append(np.concatenate([lead, vals], axis=1))
+    tiles = np.concatenate(tiles)
+    kv_c, k_pe = _tokens_from_tiles(tiles, 43)
+    _insert_and_compare(kv_c, k_pe, "maxima sweep")
+
+
 def test_encoder_tile_maximum_through_every_bf16_exponent():
     """Tiles whose maximum magnitude is m * 2^e for every bf16 exponent e
     (subnormal maxima 2^-133 .. 2^-127 included, up to the largest finite
