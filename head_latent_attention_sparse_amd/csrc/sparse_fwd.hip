@@ -342,19 +342,17 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   RowRange rr;
   // A top-k selection gives every row the same length L, laid out back to
   // back (nnz = T * L), so row t most likely starts at entry t * L.  The
-  // first entries are requested at that guess together with the query,
-  // while indptr is still on its way, and used if indptr agrees; so the
-  // first gather waits for one round trip less.
+  // first entries are requested at that guess, before the query and while
+  // indptr is still on its way, and used if indptr agrees; so the first
+  // gather waits for one round trip less.
   IdxT guess_id0 = 0, guess_t0 = 0, guess_t1 = 0;
   int64_t guess_beg = -1;
   if (kSplit) {
     if (!split_plan<IdxT, kExtra>(p, s_rec, rr)) return;  // whole workgroup
-    load_query(rr.t);
   } else {
     const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
     rr.t = blockIdx.x;
     const IdxT x0 = indptr[rr.t], x1 = indptr[rr.t + 1];
-    load_query(rr.t);
     if (!kExtra && p.guess_len > 0) {
       guess_beg = rr.t * p.guess_len;
       auto at = [&](int64_t v) { return indices[guess_beg + v < p.nnz ? guess_beg + v : 0]; };
@@ -362,6 +360,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       guess_t0 = at(lane);
       guess_t1 = at(kTileKeys + lane);
     }
+    // the query after the ids: loads complete in order, so the first gather
+    // waits for indptr and its slot id, not for the query
+    load_query(rr.t);
     __builtin_amdgcn_sched_barrier(0);  // all of the above in flight before indptr is used
     clamp_range((int64_t)x0, (int64_t)x1, p.nnz, rr.beg, rr.lenp);
     int64_t lene = 0;
@@ -428,11 +429,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     if (gsub == 0) *reinterpret_cast<u32x4_t *>(dst + 64 * (kChunksPerThread - 1)) = pf[kChunksPerThread - 1];
   };
 
-  // ---- start the first tile early.  The query was requested first, then
-  // this thread's slot of tile 0 and the slots of tiles 0 and 1 (for the
-  // masks) are taken from the guess or requested now; tile 0's gather is
-  // issued as soon as its slot is in.  (The gather is conditional, so
-  // anything loaded after it would wait for it.)
+  // ---- start the first tile early.  This thread's slot of tile 0 and the
+  // slots of tiles 0 and 1 (for the masks) are taken from the guess or
+  // requested now, ahead of the query; tile 0's gather is issued as soon as
+  // its slot is in.  (The gather is conditional, so anything loaded after it
+  // would wait for it.)
   const bool guessed = guess_beg == rr.beg && rr.vb == 0 && rr.ve == p.guess_len;
   IdxT my_id0, slot_t0, slot_t1;
   if (guessed) {
@@ -443,6 +444,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     my_id0 = fetch_entry(0, grec);
     slot_t0 = fetch_entry(0, lane);
     slot_t1 = fetch_entry(1, lane);
+  }
+  if (kSplit) {
+    load_query(t);  // after the slot ids, for the same reason
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   issue_gather_slot(slot_of(my_id0, 0, grec));  // tile 0
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       s_slot[0][tid] = slot_of(slot_t0, 0, tid);
       s_slot[1][tid] = slot_of(slot_t1, 1, tid);
     }
-    store_gather();  // tile 0 (issued before the query split)
+    store_gather();  // tile 0
     __syncthreads();
     if (ntiles > 1) issue_gather(1);
     for (int k = 0; k < ntiles; ++k) {
