@@ -32,6 +32,20 @@ mla_status_t fail(mla_status_t st, const char *fmt, ...) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Whether a [rows, heads, width] view with these (non-negative) element
+// strides spans at most 2^62 elements.  No buffer is that large, and the
+// kernels' 64-bit address arithmetic must not wrap; a view past it is an
+// argument error.
+bool view_fits(int64_t rows, int64_t stride_row, int64_t heads, int64_t stride_head, int64_t width) {
+  if (rows <= 0 || heads <= 0) return true;
+  const __int128 last = (__int128)(rows - 1) * stride_row + (__int128)(heads - 1) * stride_head + width;
+  return last <= ((__int128)1 << 62);
+}
+
+// Largest pool the insert / epilogue / gather kernels address (record
+// offsets slot * 656 stay far inside 64 bits).
+constexpr int64_t kMaxPoolRecords = (int64_t)1 << 40;
+
 // Compute units of the current device (cached per device).
 int device_cus(int device) {
   static std::mutex mu;
@@ -172,6 +186,9 @@ mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_head
   if ((out_stride_token | out_stride_head) & 1)
     return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: out strides must be even (got %lld, %lld)",
                 (long long)out_stride_token, (long long)out_stride_head);
+  if (!view_fits(num_tokens, q_stride_token, num_heads, q_stride_head, MLA_QK_DIM) ||
+      !view_fits(num_tokens, out_stride_token, num_heads, out_stride_head, MLA_KV_LORA_RANK))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: q or out view spans more than 2^62 elements");
   if (record_stride != MLA_RECORD_BYTES)
     return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
                 MLA_RECORD_BYTES);
@@ -192,7 +209,7 @@ mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_head
       return fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd: negative extra size");
     if (x.num_records > INT32_MAX - 2)
       return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: extra_num_records %lld >= 2^31 - 2", (long long)x.num_records);
-    if (num_indices + x.num_indices >= MLA_MAX_INDICES)
+    if (x.num_indices >= MLA_MAX_INDICES - num_indices)  // num_indices < 2^29 here
       return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: num_indices + extra_num_indices >= 2^29");
     if (!aligned(x.records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_sparse_fwd: extra records not 16-byte aligned");
     if (!aligned(x.indptr, idx_align) || !aligned(x.indices, idx_align))
@@ -339,7 +356,11 @@ mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t n
 
 const char *mla_last_error(void) { return g_error; }
 
-const char *mla_status_string(mla_status_t st) {
+const char *mla_status_string(mla_status_t status) {
+  // A C caller may pass any int: read the argument's bits as an int rather
+  // than as the enumeration, whose value range in C++ is only 0..7.
+  int st;
+  std::memcpy(&st, &status, sizeof st);
   switch (st) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
@@ -353,14 +374,18 @@ const char *mla_status_string(mla_status_t st) {
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 
 int64_t mla_sparse_fwd_split_workgroups(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags) {
-  if (num_tokens < 0 || num_indices < 0 || num_cus < 0 || (flags & ~kKnownFlags)) return -1;
+  // the forward's own limits: beyond them no call exists to plan for
+  if (num_tokens < 0 || num_tokens > INT32_MAX - 1 || num_indices < 0 || num_indices >= MLA_MAX_INDICES ||
+      num_cus < 0 || (flags & ~kKnownFlags))
+    return -1;
   int32_t forced = 0;
   return plan_split(num_tokens, num_indices, num_cus, flags, &forced);
 }
 
 size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_indices, uint32_t flags,
                                      int device) {
-  if (num_tokens < 0 || num_indices < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS || (flags & ~kKnownFlags)) {
+  if (num_tokens < 0 || num_tokens > INT32_MAX - 1 || num_indices < 0 || num_indices >= MLA_MAX_INDICES ||
+      num_heads < 1 || num_heads > MLA_MAX_HEADS || (flags & ~kKnownFlags)) {
     fail(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_fwd_workspace_size: invalid arguments");
     return (size_t)-1;
   }
@@ -398,6 +423,9 @@ mla_status_t mla_cache_insert(const void *kv_c, int64_t kv_c_stride_token, const
     return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: record pitch %lld, only %d (unpadded) is served", (long long)record_stride,
                 MLA_RECORD_BYTES);
   if (num_records < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: num_records %lld < 0", (long long)num_records);
+  if (num_records > kMaxPoolRecords) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: num_records %lld >= 2^40", (long long)num_records);
+  if (!view_fits(num_tokens, kv_c_stride_token, 1, 0, MLA_KV_LORA_RANK) || !view_fits(num_tokens, k_pe_stride_token, 1, 0, MLA_ROPE_DIM))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: kv_c or k_pe view spans more than 2^62 elements");
   if (!aligned(kv_c, 4) || !aligned(k_pe, 4)) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: kv_c / k_pe not 4-byte aligned");
   if (!aligned(slot_mapping, 8)) return fail(MLA_ERR_INVALID_ARGUMENT, "mla_cache_insert: slot_mapping not 8-byte aligned");
   if (!aligned(kv_records, 16)) return fail(MLA_ERR_UNSUPPORTED, "mla_cache_insert: kv_records base not 16-byte aligned");
@@ -452,6 +480,15 @@ mla_status_t mla_decode_q_concat_insert(const void *ql_nope, int64_t ql_stride_t
     if (!aligned(positions, 8) || !aligned(cos_sin_cache, 4))
       return fail(MLA_ERR_INVALID_ARGUMENT, "%s: misaligned positions or cos_sin_cache", fn);
   }
+  if (num_records > kMaxPoolRecords) return fail(MLA_ERR_UNSUPPORTED, "%s: num_records %lld >= 2^40", fn, (long long)num_records);
+  if (positions && max_position > ((int64_t)1 << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: max_position %lld >= 2^40", fn, (long long)max_position);
+  if (!view_fits(num_tokens, ql_stride_token, num_heads, ql_stride_head, MLA_KV_LORA_RANK) ||
+      !view_fits(num_tokens, q_pe_stride_token, num_heads, q_pe_stride_head, MLA_ROPE_DIM) ||
+      !view_fits(num_tokens, kv_c_stride_token, 1, 0, MLA_KV_LORA_RANK) ||
+      !view_fits(num_tokens, k_pe_stride_token, 1, 0, MLA_ROPE_DIM) ||
+      !view_fits(num_tokens, mqa_stride_token, num_heads, mqa_stride_head, MLA_QK_DIM))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a view spans more than 2^62 elements", fn);
   if (num_tokens == 0) return MLA_OK;
   if (num_tokens > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   if (!ql_nope || !q_pe || !kv_c || !k_pe || !slot_mapping || !mqa_q)
@@ -493,6 +530,7 @@ mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, i
   if (num_tokens < 0 || num_records < 0 || batch_size < 0 || block_table_width < 0 || block_table_stride < 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative size or stride", fn);
   if (block_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: block_size %lld < 1", fn, (long long)block_size);
+  if (block_size > ((int64_t)1 << 31)) return fail(MLA_ERR_UNSUPPORTED, "%s: block_size %lld > 2^31", fn, (long long)block_size);
   if (record_stride != MLA_RECORD_BYTES)
     return fail(MLA_ERR_UNSUPPORTED, "%s: record pitch %lld, only %d (unpadded) is served", fn, (long long)record_stride,
                 MLA_RECORD_BYTES);
@@ -502,6 +540,10 @@ mla_status_t mla_gather_upconvert(const void *kv_records, int64_t num_records, i
   if (!aligned(block_table, 4) || !aligned(cu_seq_lens, 4) || !aligned(seq_starts, 4))
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: misaligned int32 array", fn);
   if (num_tokens == 0) return MLA_OK;
+  if (num_records > kMaxPoolRecords) return fail(MLA_ERR_UNSUPPORTED, "%s: num_records %lld >= 2^40", fn, (long long)num_records);
+  if (!view_fits(num_tokens, dst_stride_token, 1, 0, MLA_QK_DIM) ||
+      !view_fits(batch_size, block_table_stride, 1, 0, block_table_width))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: dst or block_table view spans more than 2^62 elements", fn);
   if (num_tokens > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   if (!dst) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL dst", fn);
   if (batch_size > 0 && !cu_seq_lens) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL cu_seq_lens", fn);
@@ -538,6 +580,10 @@ mla_status_t v_up_proj_impl(const char *fn, bool prepared, const void *latent, i
   if (latent_stride_token < 0 || latent_stride_head < 0 || gate_stride_token < 0 || out_stride_token < 0 ||
       out_stride_head < 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative stride", fn);
+  if (!view_fits(num_tokens, latent_stride_token, num_heads, latent_stride_head, MLA_KV_LORA_RANK) ||
+      !view_fits(num_tokens, out_stride_token, num_heads, out_stride_head, 128) ||
+      (gate && !view_fits(num_tokens, gate_stride_token, 1, 0, (int64_t)num_heads * 128)))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a view spans more than 2^62 elements", fn);
   if (!aligned(latent, 16) || latent_stride_token % 8 || latent_stride_head % 8)
     return fail(MLA_ERR_UNSUPPORTED, "%s: latent must be 16-byte aligned with strides that are multiples of 8", fn);
   if (!aligned(out, 4) || (out_stride_token | out_stride_head) & 1 || !aligned(w_uv, prepared ? 16 : 2) ||
@@ -636,6 +682,15 @@ mla_status_t mla_prefill_key_concat_insert(void *q, int64_t q_stride_token, int6
     if (!aligned(positions, 8) || !aligned(cos_sin_cache, 4))
       return fail(MLA_ERR_INVALID_ARGUMENT, "%s: misaligned positions or cos_sin_cache", fn);
   }
+  if (num_records > kMaxPoolRecords) return fail(MLA_ERR_UNSUPPORTED, "%s: num_records %lld >= 2^40", fn, (long long)num_records);
+  if (positions && max_position > ((int64_t)1 << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: max_position %lld >= 2^40", fn, (long long)max_position);
+  if (!view_fits(num_tokens, q_stride_token, num_heads, q_stride_head, qk_nope_head_dim + MLA_ROPE_DIM) ||
+      !view_fits(num_tokens, k_nope_stride_token, num_heads, k_nope_stride_head, qk_nope_head_dim) ||
+      !view_fits(num_tokens, kv_c_stride_token, 1, 0, MLA_KV_LORA_RANK) ||
+      !view_fits(num_tokens, k_pe_stride_token, 1, 0, MLA_ROPE_DIM) ||
+      !view_fits(num_tokens, k_out_stride_token, num_heads, k_out_stride_head, qk_nope_head_dim + MLA_ROPE_DIM))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: a view spans more than 2^62 elements", fn);
   if (num_tokens == 0) return MLA_OK;
   if (num_tokens > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "%s: too many tokens", fn);
   if (!k_nope || !kv_c || !k_pe || !slot_mapping || !k_out || (positions && !q))

@@ -190,7 +190,9 @@ mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t n
  * kimi_k3 specialized-decode page are (PreparedMla.fill_splits / max_seq).
  * Without a forced chunk the chunk size is then picked on the device from
  * the actual row lengths: the smallest multiple of 64 entries (at least 512)
- * whose chunks fit that many workgroups.  Returns -1 for invalid arguments.
+ * whose chunks fit that many workgroups.  Returns -1 for invalid arguments
+ * (negative sizes, num_tokens >= 2^31 - 1 or num_indices >= 2^29, the
+ * forward's own limits, or unknown flag bits).
  */
 int64_t mla_sparse_fwd_split_workgroups(int64_t num_tokens, int64_t num_indices, int32_t num_cus, uint32_t flags);
 
@@ -198,7 +200,8 @@ int64_t mla_sparse_fwd_split_workgroups(int64_t num_tokens, int64_t num_indices,
  * mla_sparse_fwd_workspace_size - bytes of split-KV workspace a call with
  * these arguments needs on device `device` (0 when it does not split).
  * Host only; queries the device's compute-unit count once.
- * Returns (size_t)-1 on error (see mla_last_error).
+ * Returns (size_t)-1 on error (see mla_last_error): the argument limits of
+ * mla_sparse_fwd_split_workgroups, num_heads outside 1..16, or no device.
  */
 size_t mla_sparse_fwd_workspace_size(int64_t num_tokens, int32_t num_heads, int64_t num_indices,
                                      uint32_t flags, int device);

@@ -84,6 +84,8 @@ def fwd(**kw):
     (dict(indptr=None), INVALID),
     (dict(indices=None), INVALID),
     (dict(T=513, flags=2 | (4 << 16)), UNSUPPORTED),  # forced split-KV: at most 512 rows
+    (dict(qst=(1 << 62)), INVALID),                      # the q view would span past 2^62 elements
+    (dict(osh=(1 << 60)), INVALID),
 ])
 def test_fwd_rejections(kw, status):
     st, msg = fwd(**kw)
@@ -147,6 +149,10 @@ def test_split_plan_depends_only_on_host_values():
     lib = mla.lib()
     assert lib.mla_sparse_fwd_split_workgroups(-1, 0, 256, 0) == -1
     assert lib.mla_sparse_fwd_split_workgroups(8, 0, 256, 1 << 5) == -1  # unknown flag bit
+    # beyond the forward's own limits there is nothing to plan
+    assert lib.mla_sparse_fwd_split_workgroups(8, 1 << 29, 256, 0) == -1
+    assert lib.mla_sparse_fwd_split_workgroups((1 << 31) - 1, 100, 256, 0) == -1
+    assert lib.mla_sparse_fwd_split_workgroups(8, (1 << 63) - 1, 256, 1 << 16) == -1
 
 
 def test_workspace_size_of_forced_chunks_needs_no_device():
