@@ -23,6 +23,14 @@
  * written nothing; mla_last_error() then holds a message for the calling
  * thread.  Validation reads argument values only (no device reads), so a
  * rejected call is safe at any time, including during stream capture.
+ *
+ * Views: a strided view [rows, heads, width] must span at most 2^62
+ * elements, (rows - 1) * row_stride + (heads - 1) * head_stride + width,
+ * or the call returns MLA_ERR_INVALID_ARGUMENT (no buffer is that large,
+ * and the kernels' 64-bit address arithmetic must not wrap).  The insert,
+ * the epilogues and the gather serve pools of at most 2^40 records, tables
+ * of at most 2^40 positions and blocks of at most 2^31 records
+ * (MLA_ERR_UNSUPPORTED beyond).
  */
 #ifndef MLA_H
 #define MLA_H
