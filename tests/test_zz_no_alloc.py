@@ -109,3 +109,39 @@ def test_noalloc_refuses_a_split_larger_than_the_scratch():
     want = mla.sparse_fwd(q, pool, ptr, idx, SCALE, has_invalid=True, return_lse=True)
     torch.cuda.synchronize()
     same((out, lse), want, "after a refused call")
+
+
+def test_noalloc_under_graph_capture():
+    """The callers the entry point is for: a split forward captured in a HIP
+    graph with no workspace argument and no allocation, replayed three times
+    with new queries and slot ids written into the captured buffers (other
+    eager work and synchronizations between the replays).  Each replay must
+    equal the workspace entry point, run eagerly on the same inputs, bit for
+    bit."""
+    say("no-alloc forward: captured in a graph, replayed three times")
+    L = mla.lib()
+    q, pool, ptr, idx = problem(17, 32, 16, 6000, 1500, 6000)
+    t, heads = q.shape[0], q.shape[1]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mla.split_workgroups(t, idx.numel(), cus) > 0
+    out = torch.empty((t, heads, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((t, heads), dtype=torch.float32, device=DEV)
+    st, _, _ = noalloc(q, pool, ptr, idx, out=out, lse=lse)  # first call on the device: eager
+    assert st == 0, L.mla_last_error().decode()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st, _, _ = noalloc(q, pool, ptr, idx, out=out, lse=lse)
+    assert st == 0, L.mla_last_error().decode()
+    g = torch.Generator().manual_seed(18)
+    for rep in range(3):
+        q.copy_(torch.randn(q.shape, generator=g).to(torch.bfloat16))
+        idx.copy_(torch.randint(-1, pool.shape[0], idx.shape, generator=g, dtype=torch.int32))
+        noise = torch.randn((1 << 20,), device=DEV).abs().sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = mla.sparse_fwd(q, pool, ptr, idx, SCALE, has_invalid=True, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        same((out, lse), want, f"replay {rep}")
