@@ -701,10 +701,12 @@ def bench_insert(args, dev):
 def bench_decode_step(args, dev):
     """One decode step of 64 requests, H = 16, over the paged decode
     workload's pool and CSR lists: mla_decode_q_concat_insert (mqa_q with
-    RoPE, the new tokens' records), mla_sparse_fwd (split-KV pass and merge)
-    and mla_v_up_proj with the gate.  Timed eagerly and as one captured HIP
-    graph replayed per step, and as one graph of ten steps; `value` takes
-    the fastest of the three."""
+    RoPE, the new tokens' records), then the attention and the gated W_UV
+    up-projection, either as mla_sparse_fwd (split-KV pass and merge) plus
+    mla_v_up_proj_prepared, or as mla_sparse_fwd_v_up_proj (the projection
+    fused into the merge).  Each is timed eagerly, as one captured HIP graph
+    replayed per step, and as one graph of ten steps; `value` takes the
+    fastest."""
     import torch
 
     import head_latent_attention_sparse_amd as mla
@@ -730,35 +732,46 @@ def bench_decode_step(args, dev):
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step():
+    def step_separate():
         mla.decode_q_concat_insert(ql, qp, kv, kp, view, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
         mla.sparse_fwd(mqa, view, indptr, indices, w.softmax_scale, out=out, return_lse=True, workspace=workspace)
         mla.v_up_proj(out, w_uv, gate=gate, out=vout, prepared=True)
 
+    def step_fused():
+        mla.decode_q_concat_insert(ql, qp, kv, kp, view, slots, positions=pos, cos_sin_cache=table, mqa_q=mqa)
+        mla.sparse_fwd_v_up_proj(mqa, view, indptr, indices, w.softmax_scale, w_uv, gate=gate, out=out, v_out=vout,
+                                 return_lse=True, workspace=workspace)
+
     stream = torch.cuda.current_stream(dev)
-    eager_ms, eager_dev = time_steps(step, args, stream)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    graph_ms, graph_dev = time_steps(graph.replay, args, torch.cuda.current_stream(dev))
-    # ten steps in one graph: per-replay costs spread over ten steps
-    graph10 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph10):
-        for _ in range(10):
+    timings = {}
+    for name, step in (("separate", step_separate), ("fused", step_fused)):
+        eager = time_steps(step, args, stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
             step()
-    torch.cuda.synchronize()
-    g10_ms, g10_dev = time_steps(graph10.replay, args, torch.cuda.current_stream(dev))
-    g10_ms, g10_dev = g10_ms / 10, g10_dev / 10
-    assert torch.isfinite(vout.float()).all(), "non-finite output"
+        torch.cuda.synchronize()
+        one = time_steps(graph.replay, args, torch.cuda.current_stream(dev))
+        # ten steps in one graph: per-replay costs spread over ten steps
+        graph10 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph10):
+            for _ in range(10):
+                step()
+        torch.cuda.synchronize()
+        ten = time_steps(graph10.replay, args, torch.cuda.current_stream(dev))
+        timings[name] = {"eager": eager, "graph": one, "graph10": (ten[0] / 10, ten[1] / 10)}
+        assert torch.isfinite(vout.float()).all(), "non-finite output"
 
     written = int((e.slots >= 0).sum())
     moved = (w.nnz_valid() * 656.0                      # records gathered
              + b * h * (512 + 64) * 2 + b * (512 + 64) * 2 + written * 656  # epilogue reads, records written
              + b * h * 576 * 2 * 2                      # mqa_q written, then read by the forward
-             + b * h * 512 * 2 * 2                      # out written, then read by the up-projection
+             + b * h * 512 * 2                          # the attention output written
              + w_uv.numel() * 2 + gate.numel() * 2 + vout.numel() * 2)
-    best_ms, best_dev = min((eager_ms, eager_dev), (graph_ms, graph_dev), (g10_ms, g10_dev), key=lambda x: x[1])
+    best_name, best_mode = min(((n, m) for n in timings for m in timings[n]), key=lambda nm: timings[nm[0]][nm[1]][1])
+    best_ms, best_dev = timings[best_name][best_mode]
+    eager_ms, eager_dev = timings["fused"]["eager"]
+    graph_ms, graph_dev = timings["fused"]["graph"]
+    g10_ms, g10_dev = timings["fused"]["graph10"]
     achieved = moved / (best_dev * 1e-3) / 1e9
     result = {
         "metric": "MLA decode step (epilogue + split-KV sparse forward + W_UV up-projection): steps/s",
@@ -777,17 +790,20 @@ def bench_decode_step(args, dev):
                                f"of {w.num_records} records, RoPE, gated up-projection",
                    "parallelism": "single GPU"},
         "device_ms_per_step": best_dev,
+        "best": f"{best_name}, {best_mode}",
         "eager_ms_per_step": eager_ms,
         "eager_device_ms_per_step": eager_dev,
         "graph_ms_per_step": graph_ms,
         "graph_device_ms_per_step": graph_dev,
         "graph10_ms_per_step": g10_ms,
         "graph10_device_ms_per_step": g10_dev,
+        "device_ms_per_step_by_variant": {n: {m: timings[n][m][1] for m in timings[n]} for n in timings},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_launch": moved},
     }
-    log(f"device us/step: eager {eager_dev * 1e3:.1f}, graph of one step {graph_dev * 1e3:.1f}, "
-        f"graph of ten steps {g10_dev * 1e3:.1f}")
+    for n in timings:
+        log(f"{n}: device us/step eager {timings[n]['eager'][1] * 1e3:.1f}, graph of one step "
+            f"{timings[n]['graph'][1] * 1e3:.1f}, graph of ten steps {timings[n]['graph10'][1] * 1e3:.1f}")
     print(json.dumps(result), flush=True)
 
 

@@ -23,5 +23,6 @@ from .ops import (  # noqa: F401
     prepare_w_uv,
     split_workgroups,
     sparse_fwd,
+    sparse_fwd_v_up_proj,
     v_up_proj,
 )

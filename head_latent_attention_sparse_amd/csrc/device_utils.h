@@ -72,4 +72,13 @@ __device__ __forceinline__ float xor_shuffle(float v, int mask) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
 }
 
+// Job of workgroup `id` in a grid of 8 * ceil(jobs / 8) workgroups: the
+// dispatcher hands workgroups to the 8 XCDs round-robin (XCD id % 8), so
+// this gives each XCD a contiguous run of jobs; neighbouring jobs (the same
+// head's rows, say) then share that XCD's L2.  A result >= jobs means no job.
+__device__ __forceinline__ int64_t xcd_job(int64_t id, int64_t jobs) {
+  return (id % 8) * ((jobs + 7) / 8) + id / 8;
+}
+inline int64_t xcd_grid(int64_t jobs) { return 8 * ((jobs + 7) / 8); }
+
 }  // namespace mla

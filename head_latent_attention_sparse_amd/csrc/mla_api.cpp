@@ -166,6 +166,13 @@ struct FwdExtra {
   int64_t num_records = 0, record_stride = MLA_RECORD_BYTES;
   const void *indptr = nullptr, *indices = nullptr;
   int64_t num_indices = 0;
+  // the gated up-projection on prepared weights (mla_sparse_fwd_v_up_proj):
+  // fused into the merge of a split call, launched after the forward otherwise
+  const void *vp_w = nullptr;
+  const void *vp_gate = nullptr;
+  int64_t vp_gate_st = 0;
+  void *vp_out = nullptr;
+  int64_t vp_st = 0, vp_sh = 0;
 };
 
 mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
@@ -302,8 +309,33 @@ mla_status_t sparse_fwd_impl(const void *q, int64_t num_tokens, int32_t num_head
     a.ws_lse = reinterpret_cast<float *>(base + l.lse_off);
     a.ws_prefix = reinterpret_cast<int32_t *>(base + l.prefix_off);
   }
+  if (x.vp_w) {
+    a.vp_w = static_cast<const uint16_t *>(x.vp_w);
+    a.vp_gate = static_cast<const uint16_t *>(x.vp_gate);
+    a.vp_gate_st = x.vp_gate_st;
+    a.vp_out = static_cast<uint16_t *>(x.vp_out);
+    a.vp_st = x.vp_st;
+    a.vp_sh = x.vp_sh;
+  }
   hipError_t e = mla::launch_sparse_fwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd: launch failed: %s", hipGetErrorString(e));
+  if (x.vp_w && bound <= 0) {  // no merge to fuse into: project the forward's output
+    mla::VUpProjArgs v;
+    v.latent = static_cast<const uint16_t *>(out);
+    v.lat_st = out_stride_token;
+    v.lat_sh = out_stride_head;
+    v.w = static_cast<const uint16_t *>(x.vp_w);
+    v.gate = static_cast<const uint16_t *>(x.vp_gate);
+    v.gate_st = x.vp_gate_st;
+    v.num_tokens = num_tokens;
+    v.num_heads = num_heads;
+    v.out = static_cast<uint16_t *>(x.vp_out);
+    v.out_st = x.vp_st;
+    v.out_sh = x.vp_sh;
+    v.w_prepared = true;
+    e = mla::launch_v_up_proj(v, device_cus(device), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_sparse_fwd_v_up_proj: launch failed: %s", hipGetErrorString(e));
+  }
   return MLA_OK;
 }
 
@@ -352,6 +384,45 @@ mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t n
   return sparse_fwd_impl(q, num_tokens, num_heads, q_stride_token, q_stride_head, kv_records, num_records,
                          record_stride, kv_indptr, kv_indices, num_indices, softmax_scale, flags, out,
                          out_stride_token, out_stride_head, lse, nullptr, 0, stream, x);
+}
+
+mla_status_t mla_sparse_fwd_v_up_proj(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                                      int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                                      int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                                      int64_t num_indices, float softmax_scale, uint32_t flags, void *out,
+                                      int64_t out_stride_token, int64_t out_stride_head, float *lse,
+                                      const void *w_uv_prepared, const void *gate, int64_t gate_stride_token,
+                                      void *v_out, int64_t v_out_stride_token, int64_t v_out_stride_head,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "mla_sparse_fwd_v_up_proj";
+  // the projection's own conditions first (the forward checks the rest)
+  if (num_tokens < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "%s: num_tokens %lld < 0", fn, (long long)num_tokens);
+  if (num_tokens > INT32_MAX - 1) return fail(MLA_ERR_UNSUPPORTED, "%s: num_tokens %lld too large", fn, (long long)num_tokens);
+  if (out_stride_token < 0 || out_stride_head < 0 || gate_stride_token < 0 || v_out_stride_token < 0 ||
+      v_out_stride_head < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: negative stride", fn);
+  if (!aligned(out, 16) || out_stride_token % 8 || out_stride_head % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: out must be 16-byte aligned with strides that are multiples of 8", fn);
+  if (!aligned(w_uv_prepared, 16)) return fail(MLA_ERR_UNSUPPORTED, "%s: prepared weights not 16-byte aligned", fn);
+  if (!aligned(v_out, 4) || ((v_out_stride_token | v_out_stride_head) & 1) ||
+      (gate && (!aligned(gate, 4) || (gate_stride_token & 1))))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: v_out / gate must be 4-byte aligned with even strides", fn);
+  if (num_heads >= 1 && num_heads <= MLA_MAX_HEADS &&
+      (!view_fits(num_tokens, v_out_stride_token, num_heads, v_out_stride_head, 128) ||
+       (gate && !view_fits(num_tokens, gate_stride_token, 1, 0, (int64_t)num_heads * 128))))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: v_out or gate view spans more than 2^62 elements", fn);
+  if (num_tokens > 0 && (!w_uv_prepared || !v_out))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "%s: NULL w_uv_prepared or v_out", fn);
+  FwdExtra x;
+  x.vp_w = w_uv_prepared;
+  x.vp_gate = gate;
+  x.vp_gate_st = gate_stride_token;
+  x.vp_out = v_out;
+  x.vp_st = v_out_stride_token;
+  x.vp_sh = v_out_stride_head;
+  return sparse_fwd_impl(q, num_tokens, num_heads, q_stride_token, q_stride_head, kv_records, num_records,
+                         record_stride, kv_indptr, kv_indices, num_indices, softmax_scale, flags, out,
+                         out_stride_token, out_stride_head, lse, workspace, workspace_bytes, stream, x);
 }
 
 const char *mla_last_error(void) { return g_error; }

@@ -41,6 +41,14 @@ struct FwdArgs {
   const void *extra_indices = nullptr;
   int64_t extra_num_indices = 0;
   const float *sink = nullptr;
+  // Optional up-projection fused into the merge of a split call (prepared
+  // W_UV, no sink, no second segment); a call that does not split leaves
+  // the projection to the caller.
+  const uint16_t *vp_w = nullptr;
+  const uint16_t *vp_gate = nullptr;
+  int64_t vp_gate_st = 0;
+  uint16_t *vp_out = nullptr;
+  int64_t vp_st = 0, vp_sh = 0;
 };
 
 hipError_t launch_sparse_fwd(const FwdArgs &a, hipStream_t stream);
@@ -133,9 +141,33 @@ struct VUpProjArgs {
   uint16_t *out;           // bf16, element (t, h, v) at t*out_st + h*out_sh + v
   int64_t out_st, out_sh;
   bool w_prepared = false;  // w holds launch_prepare_w_uv's fragment order
+  int32_t parts = 0;        // row-tile workgroups per head (set by launch_v_up_proj)
 };
 
 hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t stream);
+
+// The split-KV merge fused with the up-projection on prepared weights: each
+// row's chunk partials are merged exactly as merge_kernel merges them with
+// `lanes` chunk lanes (bit for bit), the merged latent row is written to
+// `out` as bf16 (and the LSE), and the same bf16 row goes straight into the
+// projection, which computes what v_up_proj_kernel<gate, prepared> computes
+// (bit for bit).
+struct MergeVUpProjArgs {
+  const float *ws_out;       // [chunks, H, 512] float32 partials
+  const float *ws_lse;       // [chunks, H] base-2 LSEs
+  const int32_t *ws_prefix;  // [T + 1] first chunk of each row
+  int32_t num_tokens;
+  int32_t num_heads;
+  uint16_t *out;  // merged latent, element (t, h, l) at t*out_st + h*out_sh + l
+  int64_t out_st, out_sh;
+  float *lse;                 // [T, H] natural log, or nullptr
+  const uint16_t *w_prepared;  // W_UV in launch_prepare_w_uv's order
+  const uint16_t *gate;        // element (t, 128h + v) at t*gate_st + 128h + v, or nullptr
+  int64_t gate_st;
+  uint16_t *v_out;  // element (t, h, v) at t*v_st + h*v_sh + v
+  int64_t v_st, v_sh;
+};
+hipError_t launch_merge_v_up_proj(const MergeVUpProjArgs &a, int lanes, hipStream_t stream);
 // W_UV [H, 512, 128] bf16 -> the same bytes in the up-projection's fragment order
 hipError_t launch_prepare_w_uv(const uint16_t *w, uint16_t *w_prepared, int32_t num_heads, hipStream_t stream);
 

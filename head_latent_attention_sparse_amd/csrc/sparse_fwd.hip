@@ -36,6 +36,7 @@
 //    back (a top-k selection), each workgroup fetches its first slot ids at
 //    the guessed row start while its indptr pair is still in flight.
 #include "device_utils.h"
+#include "merge_acc.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -627,21 +628,6 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
 constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 8;  // chunks per thread with their loads in flight together
 
-struct MergeAcc {
-  float m, l;      // running max (log2 domain) and sum of 2^(lse - m)
-  floatx4_t o;     // running sum of 2^(lse - m) o
-};
-
-__device__ __forceinline__ void merge_add(MergeAcc &a, float lse, const floatx4_t &o) {
-  if (lse == -INFINITY) return;  // an empty partial weighs 0
-  const float m = fmaxf(a.m, lse);
-  const float sa = a.m == -INFINITY ? 0.f : fast_exp2(a.m - m);
-  const float w = fast_exp2(lse - m);
-  a.l = a.l * sa + w;
-  a.o = a.o * sa + o * w;
-  a.m = m;
-}
-
 template <bool kLse, int kLanes>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse,
                                                               const int32_t *prefix, int32_t heads, uint16_t *out,
@@ -663,7 +649,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
   const int col = part * 4 * kQuads + 4 * cq;
   const float *op = ws_out + (c0 * heads + h) * kLatent + col;  // chunk s at op[s * heads * 512]
 
-  MergeAcc acc = {-INFINITY, 0.f, floatx4_t{0.f, 0.f, 0.f, 0.f}};
+  MergeAcc acc = merge_acc_empty();
   for (int base = cl; base < nc; base += kLanes * kMergeBatch) {
     float ls[kMergeBatch];
     floatx4_t os[kMergeBatch];
@@ -684,16 +670,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
     // the sink: one more term with a zero value
     if (sink) merge_add(acc, sink[h] * kLog2e, floatx4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int k = 1; k < kLanes; ++k) {
-      const MergeAcc b = s_acc[k][cq];
-      if (b.m == -INFINITY) continue;
-      const float m = fmaxf(acc.m, b.m);
-      const float sa = acc.m == -INFINITY ? 0.f : fast_exp2(acc.m - m);
-      const float sb = fast_exp2(b.m - m);
-      acc.l = acc.l * sa + b.l * sb;
-      acc.o = acc.o * sa + b.o * sb;
-      acc.m = m;
-    }
+    for (int k = 1; k < kLanes; ++k) merge_combine(acc, s_acc[k][cq]);
     const float inv = acc.l > 0.f ? 1.f / acc.l : 0.f;
     uint32_t *dst = reinterpret_cast<uint32_t *>(out + t * o_st + (int64_t)h * o_sh + col);
     dst[0] = pack_bf16x2(acc.o[0] * inv, acc.o[1] * inv);
@@ -760,9 +737,29 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   // chunk lanes for the average chunks per row (one batch of loads each when they fit)
   const int64_t per_row = (a.chunk_bound + a.num_tokens - 1) / a.num_tokens;
-  if (per_row <= 2 * kMergeBatch)
+  const int lanes = per_row <= 2 * kMergeBatch ? 2 : (per_row <= 4 * kMergeBatch ? 4 : 8);
+  if (a.vp_w) {
+    MergeVUpProjArgs m;
+    m.ws_out = a.ws_out;
+    m.ws_lse = a.ws_lse;
+    m.ws_prefix = a.ws_prefix;
+    m.num_tokens = a.num_tokens;
+    m.num_heads = a.num_heads;
+    m.out = a.out;
+    m.out_st = a.out_stride_token;
+    m.out_sh = a.out_stride_head;
+    m.lse = a.lse;
+    m.w_prepared = a.vp_w;
+    m.gate = a.vp_gate;
+    m.gate_st = a.vp_gate_st;
+    m.v_out = a.vp_out;
+    m.v_st = a.vp_st;
+    m.v_sh = a.vp_sh;
+    return launch_merge_v_up_proj(m, lanes, stream);
+  }
+  if (lanes == 2)
     launch_merge<2>(a, stream);
-  else if (per_row <= 4 * kMergeBatch)
+  else if (lanes == 4)
     launch_merge<4>(a, stream);
   else
     launch_merge<8>(a, stream);

@@ -22,6 +22,7 @@
 // float32 result is staged in LDS, so the gate is applied and the output
 // written in coalesced 16-byte pieces.
 #include "device_utils.h"
+#include "merge_acc.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -58,7 +59,12 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y;
+  // job = (head, part): a head's parts share an XCD and its copy of W_UV[h]
+  const int64_t jobs = (int64_t)a.parts * a.num_heads;
+  const int64_t job = xcd_job(blockIdx.x, jobs);
+  if (job >= jobs) return;  // whole workgroup
+  const int h = (int)(job / a.parts);
+  const int64_t part = job - (int64_t)h * a.parts;
   const int64_t tiles = (a.num_tokens + kTileRows - 1) / kTileRows;
 
   // ---- tile loads.  Latent chunk q = tid + 256k of the tile's 32 x 64
@@ -88,9 +94,9 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
   };
 
   // the first two tiles load while the weights are set up
-  const int64_t step = gridDim.x;
+  const int64_t step = a.parts;
   TileRegs r0, r1;
-  int64_t tile = blockIdx.x;
+  int64_t tile = part;
   load_tile(tile, r0);
   load_tile(tile + step, r1);
 
@@ -244,6 +250,138 @@ __global__ __launch_bounds__(kThreads, 1) void v_up_proj_kernel(VUpProjArgs a) {
   }
 }
 
+// ---- The split-KV merge fused with the up-projection on prepared weights.
+// A workgroup of eight waves takes kFRows = 4 rows of one head.  Merge:
+// thread (row tid / 128, column quad tid % 128) merges its chunk partials
+// into kLanes accumulators, chunk s into accumulator s % kLanes in
+// increasing s, then folds accumulators 1.. into 0: the order
+// merge_kernel<kLanes> uses (with the same fused multiply-adds), so the
+// merged bf16 row is that kernel's.  The row goes to `out` and, as the same
+// bf16 values, into the LDS A tile (rows 4..15 zero); wave w' then
+// multiplies by the 16 columns 16w' .. 16w'+15 of W_UV[h] (its B fragments
+// in registers: fragment j = w' % 2 of v_up_proj_kernel's wave w' / 2,
+// k-steps in that kernel's order) and applies the gate as that kernel does.
+// Rows past the end load nothing and store nothing.
+constexpr int kFThreads = 512;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFRows = kFThreads / 128;  // one (row, column quad) per thread
+constexpr int kFBatch = 8;               // chunks with their loads in flight together
+static_assert(kFRows <= 16 && kFWaves * 16 == kV, "one MFMA row tile, 16 columns per wave");
+
+template <bool kGate, bool kLse, int kLanes>
+__global__ __launch_bounds__(kFThreads, 1) void merge_v_up_proj_kernel(MergeVUpProjArgs a) {
+  static_assert(kFBatch % kLanes == 0, "a batch starts at chunk lane 0");
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[16 * kAPitch];
+  __shared__ __attribute__((aligned(16))) float s_o[kFRows * kOPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  // job = (head, row block): a head's row blocks share an XCD and its copy of W_UV[h]
+  const int64_t blocks = (a.num_tokens + kFRows - 1) / kFRows;
+  const int64_t jobs = blocks * a.num_heads;
+  const int64_t job = xcd_job(blockIdx.x, jobs);
+  if (job >= jobs) return;  // whole workgroup
+  const int h = (int)(job / blocks);
+  const int64_t row0 = (job - (int64_t)h * blocks) * kFRows;
+
+  // this wave's 16 columns of W_UV[h] as B fragments (requested first, used last)
+  bf16x8_t bw[kKSteps];
+  {
+    const u32x4_t *wp = reinterpret_cast<const u32x4_t *>(a.w_prepared) +
+                        ((int64_t)h * kWaves + (wave >> 1)) * (kKSteps * 2 * 64) + (wave & 1) * 64 + lane;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) bw[s] = as_bf16x8(wp[s * 2 * 64]);
+  }
+  // the storing threads' gate words, requested now rather than after the projection
+  uint32_t gate_w[4] = {0u, 0u, 0u, 0u};
+  if (kGate && tid < kFRows * 16 && row0 + (tid >> 4) < a.num_tokens) {
+    const uint32_t *gp =
+        reinterpret_cast<const uint32_t *>(a.gate + (row0 + (tid >> 4)) * a.gate_st + (int64_t)h * kV + 8 * (tid & 15));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gate_w[i] = gp[i];
+  }
+  for (int i = tid; i < (16 - kFRows) * kAPitch / 8; i += kFThreads)
+    reinterpret_cast<u32x4_t *>(s_a + kFRows * kAPitch)[i] = u32x4_t{0u, 0u, 0u, 0u};
+
+  // ---- merge
+  {
+    const int r = tid >> 7, cq = tid & 127;
+    const int64_t t = row0 + r;
+    int32_t c0 = 0, nc = 0;
+    if (t < a.num_tokens) {
+      c0 = a.ws_prefix[t];
+      nc = a.ws_prefix[t + 1] - c0;
+    }
+    const float *lp = a.ws_lse + (int64_t)c0 * a.num_heads + h;                     // chunk s at lp[s * H]
+    const float *op = a.ws_out + ((int64_t)c0 * a.num_heads + h) * kLatent + 4 * cq;  // at op[s * H * 512]
+    MergeAcc acc[kLanes];
+#pragma unroll
+    for (int l = 0; l < kLanes; ++l) acc[l] = merge_acc_empty();
+    for (int base = 0; base < nc; base += kFBatch) {
+      float ls[kFBatch];
+      floatx4_t os[kFBatch];
+#pragma unroll
+      for (int j = 0; j < kFBatch; ++j) {
+        const int s = base + j;
+        const int sc = s < nc ? s : base;  // in range: base < nc
+        ls[j] = lp[(int64_t)sc * a.num_heads];
+        os[j] = *reinterpret_cast<const floatx4_t *>(op + (int64_t)sc * a.num_heads * kLatent);
+        if (s >= nc) ls[j] = -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kFBatch; ++j) merge_add(acc[j % kLanes], ls[j], os[j]);
+    }
+#pragma unroll
+    for (int l = 1; l < kLanes; ++l) merge_combine(acc[0], acc[l]);
+    const float inv = acc[0].l > 0.f ? 1.f / acc[0].l : 0.f;
+    const uint32_t lo = pack_bf16x2(acc[0].o[0] * inv, acc[0].o[1] * inv);
+    const uint32_t hi = pack_bf16x2(acc[0].o[2] * inv, acc[0].o[3] * inv);
+    *reinterpret_cast<u32x2_t *>(s_a + r * kAPitch + 4 * cq) = u32x2_t{lo, hi};
+    if (t < a.num_tokens) {
+      uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + t * a.out_st + (int64_t)h * a.out_sh + 4 * cq);
+      dst[0] = lo;
+      dst[1] = hi;
+      if (kLse && cq == 0)
+        a.lse[t * a.num_heads + h] = acc[0].m == -INFINITY ? -INFINITY : (acc[0].m + fast_log2(acc[0].l)) * kLn2;
+    }
+  }
+  __syncthreads();
+
+  // ---- projection: rows 16 (kFRows real) x columns 16 * wave + c
+  floatx4_t acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kKSteps; ++s) {
+    const bf16x8_t af = as_bf16x8(*reinterpret_cast<const u32x4_t *>(s_a + c * kAPitch + 32 * s + 8 * g));
+    acc2 = mfma_16x16x32_bf16(af, bw[s], acc2);
+  }
+  // D: lane (c, g) holds rows 4g + i, column 16 * wave + c
+  if (4 * g < kFRows) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i < kFRows) s_o[(4 * g + i) * kOPitch + 16 * wave + c] = acc2[i];
+  }
+  __syncthreads();
+  if (tid < kFRows * 16) {
+    const int rr = tid >> 4, ch = tid & 15;
+    const int64_t t = row0 + rr;
+    if (t < a.num_tokens) {
+      const floatx4_t y0 = *reinterpret_cast<const floatx4_t *>(s_o + rr * kOPitch + 8 * ch);
+      const floatx4_t y1 = *reinterpret_cast<const floatx4_t *>(s_o + rr * kOPitch + 8 * ch + 4);
+      float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      if (kGate) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t gw = gate_w[i];
+          y[2 * i] *= __builtin_amdgcn_rcpf(1.0f + __expf(-as_float(gw << 16)));
+          y[2 * i + 1] *= __builtin_amdgcn_rcpf(1.0f + __expf(-as_float(gw & 0xFFFF0000u)));
+        }
+      }
+      uint32_t *dst = reinterpret_cast<uint32_t *>(a.v_out + t * a.v_st + (int64_t)h * a.v_sh + 8 * ch);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+    }
+  }
+}
+
 // W_UV in the kernel's B-fragment order: fragment (h, w, s, j) of lane
 // (c, g) = rows 32s + 8g .. +7 of column 32w + 16j + c of W_UV[h], 8 bf16
 // values (row order, the first in the low half), stored as 16 bytes at
@@ -273,17 +411,46 @@ hipError_t launch_v_up_proj(const VUpProjArgs &a, int num_cus, hipStream_t strea
   // one workgroup per CU in all (each holds a head's weights in registers)
   int64_t per_head = (num_cus > 0 ? num_cus : 256) / a.num_heads;
   per_head = per_head < 1 ? 1 : (per_head > tiles ? tiles : per_head);
-  const dim3 grid((unsigned)per_head, (unsigned)a.num_heads);
+  VUpProjArgs k = a;
+  k.parts = (int32_t)per_head;
+  const dim3 grid((unsigned)xcd_grid(per_head * a.num_heads));
   if (a.w_prepared) {
     if (a.gate)
-      v_up_proj_kernel<true, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+      v_up_proj_kernel<true, true><<<grid, dim3(kThreads), 0, stream>>>(k);
     else
-      v_up_proj_kernel<false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+      v_up_proj_kernel<false, true><<<grid, dim3(kThreads), 0, stream>>>(k);
   } else {
     if (a.gate)
-      v_up_proj_kernel<true, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+      v_up_proj_kernel<true, false><<<grid, dim3(kThreads), 0, stream>>>(k);
     else
-      v_up_proj_kernel<false, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+      v_up_proj_kernel<false, false><<<grid, dim3(kThreads), 0, stream>>>(k);
+  }
+  return hipGetLastError();
+}
+
+template <bool kGate, bool kLse>
+void launch_merge_v_up_proj_lanes(const MergeVUpProjArgs &a, int lanes, hipStream_t stream) {
+  const dim3 grid((unsigned)xcd_grid((int64_t)((a.num_tokens + kFRows - 1) / kFRows) * a.num_heads));
+  if (lanes == 2)
+    merge_v_up_proj_kernel<kGate, kLse, 2><<<grid, dim3(kFThreads), 0, stream>>>(a);
+  else if (lanes == 4)
+    merge_v_up_proj_kernel<kGate, kLse, 4><<<grid, dim3(kFThreads), 0, stream>>>(a);
+  else
+    merge_v_up_proj_kernel<kGate, kLse, 8><<<grid, dim3(kFThreads), 0, stream>>>(a);
+}
+
+hipError_t launch_merge_v_up_proj(const MergeVUpProjArgs &a, int lanes, hipStream_t stream) {
+  if (lanes != 2 && lanes != 4 && lanes != 8) return hipErrorInvalidValue;
+  if (a.gate) {
+    if (a.lse)
+      launch_merge_v_up_proj_lanes<true, true>(a, lanes, stream);
+    else
+      launch_merge_v_up_proj_lanes<true, false>(a, lanes, stream);
+  } else {
+    if (a.lse)
+      launch_merge_v_up_proj_lanes<false, true>(a, lanes, stream);
+    else
+      launch_merge_v_up_proj_lanes<false, false>(a, lanes, stream);
   }
   return hipGetLastError();
 }

@@ -45,6 +45,8 @@ SIGNATURES = {
                                  _I64, _F32, _U32, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "mla_sparse_fwd_noalloc": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P, _I64,
                                       _I64, _P, _P]),
+    "mla_sparse_fwd_v_up_proj": (_I32, [_P, _I64, _I32, _I64, _I64, _P, _I64, _I64, _P, _P, _I64, _F32, _U32, _P,
+                                        _I64, _I64, _P, _P, _P, _I64, _P, _I64, _I64, _P, _SZ, _P]),
     "mla_sparse_fwd_split_workgroups": (_I64, [_I64, _I64, _I32, _U32]),
     "mla_sparse_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _U32, ctypes.c_int]),
     "mla_workspace_reserve": (_I32, [ctypes.c_int, _SZ]),
@@ -142,21 +144,8 @@ def split_workgroups(num_tokens, num_indices, num_cus, chunk_tiles=0):
     return lib().mla_sparse_fwd_split_workgroups(num_tokens, num_indices, num_cus, chunk_tiles << CHUNK_SHIFT)
 
 
-def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid=False, out=None,
-               return_lse=False, chunk_tiles=0, workspace=None, attn_sink=None, extra_kv=None,
-               extra_indptr=None, extra_indices=None):
-    """Sparse MLA forward over fp8_ds_mla records -> (out, lse or None).
-
-    q [T, H, 576] bf16 (H <= 16, stride(2) == 1); kv_cache a record pool
-    view; kv_indptr [T + 1] and kv_indices [nnz] int32 or int64 (the same
-    dtype, contiguous); out optional [T, H, >= 512] bf16.  ``chunk_tiles``
-    forces split-KV with chunks of that many 64-key tiles (0 = the library's
-    plan).  ``workspace`` optionally supplies the split partial buffer (a
-    CUDA uint8 tensor).  ``attn_sink`` (float32 [H]) adds a per-head sink
-    logit; ``extra_kv`` / ``extra_indptr`` / ``extra_indices`` give a second
-    record pool and CSR list attended jointly with the first
-    (mla_sparse_fwd_ex).
-    """
+def _fwd_query_and_lists(q, kv_indptr, kv_indices):
+    """The forward's checks of q and the CSR lists; returns (T, H)."""
     if not (torch.is_tensor(q) and q.is_cuda and q.ndim == 3 and q.dtype == torch.bfloat16):
         raise ValueError("q must be a CUDA bf16 tensor [T, H, 576]")
     t_count, heads, dqk = q.shape
@@ -173,6 +162,45 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
         raise ValueError("kv_indptr and kv_indices must have the same dtype")
     if kv_indptr.numel() != t_count + 1:
         raise ValueError("kv_indptr must have T + 1 entries")
+    return t_count, heads
+
+
+def _fwd_workspace(L, q, t_count, heads, total_nnz, flags, workspace):
+    """The split workspace a forward call needs: (pointer, bytes, the
+    workspace tensor), pointer None and 0 bytes when the call does not
+    split.  A caller's workspace is used if large enough, else one is
+    allocated."""
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    if t_count == 0:
+        return None, 0, workspace
+    need = L.mla_sparse_fwd_workspace_size(t_count, heads, total_nnz, flags, dev)
+    if need == ctypes.c_size_t(-1).value:
+        _check(3)
+    if need == 0:
+        return None, 0, workspace
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    return workspace.data_ptr(), workspace.numel(), workspace
+
+
+def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid=False, out=None,
+               return_lse=False, chunk_tiles=0, workspace=None, attn_sink=None, extra_kv=None,
+               extra_indptr=None, extra_indices=None):
+    """Sparse MLA forward over fp8_ds_mla records -> (out, lse or None).
+
+    q [T, H, 576] bf16 (H <= 16, stride(2) == 1); kv_cache a record pool
+    view; kv_indptr [T + 1] and kv_indices [nnz] int32 or int64 (the same
+    dtype, contiguous); out optional [T, H, >= 512] bf16.  ``chunk_tiles``
+    forces split-KV with chunks of that many 64-key tiles (0 = the library's
+    plan).  ``workspace`` optionally supplies the split partial buffer (a
+    CUDA uint8 tensor).  ``attn_sink`` (float32 [H]) adds a per-head sink
+    logit; ``extra_kv`` / ``extra_indptr`` / ``extra_indices`` give a second
+    record pool and CSR list attended jointly with the first
+    (mla_sparse_fwd_ex).
+    """
+    t_count, heads = _fwd_query_and_lists(q, kv_indptr, kv_indices)
     use_extra = extra_indptr is not None or extra_indices is not None or extra_kv is not None
     if use_extra:
         if extra_kv is None or extra_indptr is None or extra_indices is None:
@@ -210,18 +238,8 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
     L = lib()
     dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
     with torch.cuda.device(dev):
-        ws_ptr, ws_bytes = None, 0
         total_nnz = kv_indices.numel() + (extra_indices.numel() if use_extra else 0)
-        if t_count > 0:
-            need = L.mla_sparse_fwd_workspace_size(t_count, heads, total_nnz, flags, dev)
-            if need == ctypes.c_size_t(-1).value:
-                _check(3)
-            if need > 0:
-                if workspace is None:
-                    workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-                if workspace.numel() < need:
-                    raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
-                ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+        ws_ptr, ws_bytes, workspace = _fwd_workspace(L, q, t_count, heads, total_nnz, flags, workspace)
         if use_extra or attn_sink is not None:
             st = L.mla_sparse_fwd_ex(
                 q.data_ptr(), t_count, heads, q.stride(0), q.stride(1),
@@ -247,6 +265,61 @@ def sparse_fwd(q, kv_cache, kv_indptr, kv_indices, softmax_scale, *, has_invalid
                 ws_ptr, ws_bytes, _stream(q.device))
     _check(st)
     return out, lse
+
+
+def sparse_fwd_v_up_proj(q, kv_cache, kv_indptr, kv_indices, softmax_scale, w_uv_prepared, *, gate=None,
+                         has_invalid=False, out=None, v_out=None, return_lse=False, chunk_tiles=0, workspace=None):
+    """sparse_fwd followed by the gated W_UV up-projection on prepared
+    weights (mla_sparse_fwd_v_up_proj) -> (v_out [T, H, 128] bf16, out, lse
+    or None).  Bit for bit what sparse_fwd then v_up_proj(prepared=True)
+    return; a call that splits merges and projects in one launch.
+
+    w_uv_prepared: prepare_w_uv's result for W_UV [H, 512, 128]; gate bf16
+    [T, H * 128] with a contiguous last dim, or None; out optional bf16
+    [T, H, >= 512] (16-byte aligned rows, strides multiples of 8); v_out
+    optional bf16 [T, H, >= 128].
+    """
+    t_count, heads = _fwd_query_and_lists(q, kv_indptr, kv_indices)
+    dev = q.device
+    if not (torch.is_tensor(w_uv_prepared) and w_uv_prepared.dtype == torch.bfloat16 and w_uv_prepared.device == dev
+            and tuple(w_uv_prepared.shape) == (heads, KV_LORA_RANK, V_HEAD_DIM) and w_uv_prepared.is_contiguous()):
+        raise ValueError(f"w_uv_prepared must be prepare_w_uv's bf16 [{heads}, 512, 128] result on q's device")
+    if gate is not None and not (torch.is_tensor(gate) and gate.dtype == torch.bfloat16 and gate.device == dev
+                                 and tuple(gate.shape) == (t_count, heads * V_HEAD_DIM) and gate.stride(1) == 1):
+        raise ValueError(f"gate must be bf16 [{t_count}, {heads * V_HEAD_DIM}] with a contiguous last dim")
+    if not (torch.is_tensor(kv_cache) and kv_cache.device == dev):
+        raise ValueError("kv cache must be on q's device")
+    kv_ptr, n_rec, pitch = _record_pool(kv_cache)
+    if out is None:
+        out = torch.empty((t_count, heads, KV_LORA_RANK), dtype=torch.bfloat16, device=dev)
+    elif not (out.dtype == torch.bfloat16 and out.device == dev and out.ndim == 3 and out.shape[0] == t_count
+              and out.shape[1] == heads and out.shape[2] >= KV_LORA_RANK and out.stride(2) == 1):
+        raise ValueError("out must be bf16 [T, H, >= 512] with stride(2) == 1 on q's device")
+    if v_out is None:
+        v_out = torch.empty((t_count, heads, V_HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    elif not (v_out.dtype == torch.bfloat16 and v_out.device == dev and v_out.ndim == 3
+              and v_out.shape[0] == t_count and v_out.shape[1] == heads and v_out.shape[2] >= V_HEAD_DIM
+              and v_out.stride(2) == 1):
+        raise ValueError("v_out must be bf16 [T, H, >= 128] with a contiguous last dim on q's device")
+    lse = torch.empty((t_count, heads), dtype=torch.float32, device=dev) if return_lse else None
+    flags = (FLAG_HAS_INVALID if has_invalid else 0) | (FLAG_RETURN_LSE if return_lse else 0)
+    if kv_indices.dtype == torch.int64:
+        flags |= FLAG_INDEX_I64
+    if not 0 <= chunk_tiles <= MAX_CHUNK_TILES:
+        raise ValueError(f"chunk_tiles must be in 0 .. {MAX_CHUNK_TILES}")
+    flags |= chunk_tiles << CHUNK_SHIFT
+    L = lib()
+    with torch.cuda.device(dev):
+        ws_ptr, ws_bytes, workspace = _fwd_workspace(L, q, t_count, heads, kv_indices.numel(), flags, workspace)
+        st = L.mla_sparse_fwd_v_up_proj(
+            q.data_ptr(), t_count, heads, q.stride(0), q.stride(1), kv_ptr, n_rec, pitch,
+            kv_indptr.data_ptr(), kv_indices.data_ptr() if kv_indices.numel() else None, kv_indices.numel(),
+            float(softmax_scale), flags, out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr() if lse is not None else None, w_uv_prepared.data_ptr(),
+            gate.data_ptr() if gate is not None else None, gate.stride(0) if gate is not None else 0,
+            v_out.data_ptr(), v_out.stride(0), v_out.stride(1), ws_ptr, ws_bytes, _stream(dev))
+    _check(st)
+    return v_out, out, lse
 
 
 def cache_insert(kv_c, k_pe, slot_mapping, kv_cache):

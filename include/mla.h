@@ -189,6 +189,44 @@ mla_status_t mla_sparse_fwd_noalloc(const void *q, int64_t num_tokens, int32_t n
                                     int64_t out_stride_token, int64_t out_stride_head, float *lse, void *stream);
 
 /*
+ * mla_sparse_fwd_v_up_proj - mla_sparse_fwd followed by the W_UV
+ * up-projection with the optional sigmoid gate, with the projection fused
+ * into the merge of a split call.
+ *
+ * The step right after the attention in MultiHeadLatentAttention
+ * (vllm.models.kimi_k3.nvidia.mla page: _v_up_proj, then the gate of
+ * forward); on the kimi_k3 specialized-decode page the value kernels
+ * (MlaValue, and DcpValue, which first merges the ranks' partials) apply it
+ * right after the attention core.  Computes exactly what
+ * mla_sparse_fwd then mla_v_up_proj_prepared compute on the same arguments,
+ * bit for bit: out and lse as mla_sparse_fwd writes them, and
+ *     v_out[t, h, v] = bf16( (sum_l out[t, h, l] * W_UV[h, l, v]) * sigmoid(gate[t, 128h + v]) )
+ * reading the bf16 `out` values.  A call that splits (see
+ * mla_sparse_fwd_split_workgroups) merges the partials and projects the
+ * merged rows in one launch, which saves the up-projection's launch and its
+ * read of `out`; a call that does not split runs the forward, then the
+ * up-projection.
+ *
+ * Arguments as for mla_sparse_fwd (no sink or second segment), except:
+ *  out          as for mla_sparse_fwd, but 16-byte aligned with strides
+ *               that are multiples of 8 elements.
+ *  w_uv_prepared  W_UV[num_heads, 512, 128] as mla_v_up_proj_prepare_weights
+ *               wrote it, 16-byte aligned.
+ *  gate         bf16 [T, num_heads * 128], row stride gate_stride_token
+ *               (even), or NULL for no gate.
+ *  v_out        bf16, element (t, h, v) at v_out + t*v_out_stride_token +
+ *               h*v_out_stride_head + v (strides even), base 4-byte aligned.
+ */
+mla_status_t mla_sparse_fwd_v_up_proj(const void *q, int64_t num_tokens, int32_t num_heads, int64_t q_stride_token,
+                                      int64_t q_stride_head, const void *kv_records, int64_t num_records,
+                                      int64_t record_stride, const void *kv_indptr, const void *kv_indices,
+                                      int64_t num_indices, float softmax_scale, uint32_t flags, void *out,
+                                      int64_t out_stride_token, int64_t out_stride_head, float *lse,
+                                      const void *w_uv_prepared, const void *gate, int64_t gate_stride_token,
+                                      void *v_out, int64_t v_out_stride_token, int64_t v_out_stride_head,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * mla_sparse_fwd_split_workgroups - the split-KV plan mla_sparse_fwd uses
  * (host only, no device access): 0 = one workgroup per row; otherwise the
  * number of workgroups of the partial pass, an upper bound on the number of
@@ -437,7 +475,7 @@ const char *mla_last_error(void);
 const char *mla_status_string(mla_status_t status);
 
 /* ABI version of this header (MLA_ABI_VERSION). */
-#define MLA_ABI_VERSION 9
+#define MLA_ABI_VERSION 10
 int32_t mla_abi_version(void);
 
 #ifdef __cplusplus

@@ -86,6 +86,12 @@ struct Fwd {
   int64_t en = 50, epitch = 656;
   const void *eptr = P, *eidx = P;
   int64_t ennz = 10;
+  // the up-projection of mla_sparse_fwd_v_up_proj
+  const void *vw = P;
+  const void *vgate = nullptr;
+  int64_t vgst = 0;
+  void *vout = P;
+  int64_t vst = 16 * 128, vsh = 128;
 };
 
 mla_status_t call_fwd(const Fwd &a) {
@@ -95,6 +101,11 @@ mla_status_t call_fwd(const Fwd &a) {
 mla_status_t call_noalloc(const Fwd &a) {
   return mla_sparse_fwd_noalloc(a.q, a.T, a.H, a.qst, a.qsh, a.kv, a.n, a.pitch, a.indptr, a.indices, a.nnz, a.scale,
                                 a.flags, a.out, a.ost, a.osh, a.lse, nullptr);
+}
+mla_status_t call_fwd_vp(const Fwd &a) {
+  return mla_sparse_fwd_v_up_proj(a.q, a.T, a.H, a.qst, a.qsh, a.kv, a.n, a.pitch, a.indptr, a.indices, a.nnz, a.scale,
+                                  a.flags, a.out, a.ost, a.osh, a.lse, a.vw, a.vgate, a.vgst, a.vout, a.vst, a.vsh,
+                                  nullptr, 0, nullptr);
 }
 mla_status_t call_fwd_ex(const Fwd &a) {
   return mla_sparse_fwd_ex(a.q, a.T, a.H, a.qst, a.qsh, a.kv, a.n, a.pitch, a.indptr, a.indices, a.nnz, a.sink,
@@ -286,6 +297,25 @@ int main() {
 
   run_cases<Fwd>("mla_sparse_fwd", Fwd{}, call_fwd, fwd_cases());
   run_cases<Fwd>("mla_sparse_fwd_noalloc", Fwd{}, call_noalloc, fwd_cases());
+  {
+    // the forward's cases through the forward + projection entry point (its
+    // own conditions hold with these placeholders), then the projection's
+    auto vp_cases = fwd_cases();
+    vp_cases.insert(vp_cases.end(), {
+        {[](Fwd &a) { a.out = P + 8; }, UNSUP},
+        {[](Fwd &a) { a.ost = 16 * 512 + 2; }, UNSUP},
+        {[](Fwd &a) { a.vw = P + 8; }, UNSUP},
+        {[](Fwd &a) { a.vout = P + 2; }, UNSUP},
+        {[](Fwd &a) { a.vsh = 129; }, UNSUP},
+        {[](Fwd &a) { a.vgate = P; a.vgst = 2049; }, UNSUP},
+        {[](Fwd &a) { a.vst = int64_t(1) << 61; }, INVALID},
+        {[](Fwd &a) { a.vw = nullptr; }, INVALID},
+        {[](Fwd &a) { a.vout = nullptr; }, INVALID},
+    });
+    // the forward's out-alignment case (P + 2) is refused for 16-byte alignment
+    // first, so its status here is the same UNSUPPORTED
+    run_cases<Fwd>("mla_sparse_fwd_v_up_proj", Fwd{}, call_fwd_vp, vp_cases);
+  }
   auto ex_cases = fwd_cases();
   ex_cases.insert(ex_cases.end(), {
       {[](Fwd &a) { a.epitch = 672; }, UNSUP},

@@ -98,6 +98,40 @@ def test_fwd_zero_tokens_is_a_no_op():
     assert st == OK
 
 
+def fwd_vp(**kw):
+    args = dict(q=A, T=4, H=16, qst=16 * 576, qsh=576, kv=A, n=100, pitch=656, indptr=A, indices=A, nnz=10,
+                scale=1.0, flags=2, out=A, ost=16 * 512, osh=512, lse=A, w=A, gate=None, gst=0, vo=A,
+                vst=16 * 128, vsh=128, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    lib = mla.lib()
+    st = lib.mla_sparse_fwd_v_up_proj(*args.values())
+    return st, lib.mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=17), UNSUPPORTED),                 # the forward's own limits still apply
+    (dict(T=-1), INVALID),
+    (dict(out=A + 8), UNSUPPORTED),            # the projection reads out 16 bytes at a time
+    (dict(ost=16 * 512 + 2), UNSUPPORTED),
+    (dict(w=A + 8), UNSUPPORTED),
+    (dict(vo=A + 2), UNSUPPORTED),
+    (dict(vsh=129), UNSUPPORTED),
+    (dict(gate=A, gst=2049), UNSUPPORTED),
+    (dict(vst=1 << 61), INVALID),
+    (dict(w=None), INVALID),
+    (dict(vo=None), INVALID),
+])
+def test_fwd_v_up_proj_rejections(kw, status):
+    st, msg = fwd_vp(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_fwd_v_up_proj_zero_tokens_is_a_no_op():
+    st, _ = fwd_vp(T=0, q=None, out=None, indptr=None, indices=None, lse=None, w=None, vo=None)
+    assert st == OK
+
+
 def insert(**kw):
     args = dict(kv_c=A, kst=512, k_pe=A, pst=64, slots=A, T=8, kv=A, n=100, pitch=656, stream=None)
     args.update(kw)
