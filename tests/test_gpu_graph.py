@@ -1,6 +1,7 @@
 """The entry points under HIP graph capture (torch.cuda.graph): a decode
 step (epilogue with RoPE and insert -> split-KV forward -> W_UV
-up-projection with gate, with plain and prepared weights) and a prefill step (key epilogue with q RoPE in
+up-projection with gate, with plain and prepared weights, and the forward
+with the projection fused into its merge) and a prefill step (key epilogue with q RoPE in
 place and insert -> plain insert -> one-workgroup-per-row forward, int64
 indices -> context gather through a block table), each
 captured once and replayed several times.  Before each replay the program
@@ -104,6 +105,9 @@ def test_decode_step_graph():
     vout = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
     w_prep = mla.prepare_w_uv(w_uv)  # once, before capture
     vout_p = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
+    out_f = torch.empty((b, h, 512), dtype=torch.bfloat16, device=DEV)  # the fused forward + projection
+    lse_f = torch.empty((b, h), dtype=torch.float32, device=DEV)
+    vout_f = torch.empty((b, h, 128), dtype=torch.bfloat16, device=DEV)
     assert mla.split_workgroups(b, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count) > 0
 
     def fresh(r):
@@ -121,10 +125,17 @@ def test_decode_step_graph():
         lse.copy_(l)
         mla.v_up_proj(out, w_uv, gate=gate, out=vout)
         mla.v_up_proj(out, w_prep, gate=gate, out=vout_p, prepared=True)
+        _, _, lf = mla.sparse_fwd_v_up_proj(mqa, pool, ip, ix, SCALE, w_prep, gate=gate, has_invalid=True, out=out_f,
+                                            v_out=vout_f, return_lse=True)
+        lse_f.copy_(lf)
 
     check_replays(step, [ql, qp, kv, kp, slots, pos, ix, gate], lambda r: [x.to(DEV) for x in fresh(r)],
-                  [mqa, out, lse, vout, vout_p], pool)
+                  [mqa, out, lse, vout, vout_p, out_f, lse_f, vout_f], pool)
     assert torch.equal(vout.view(torch.int16), vout_p.view(torch.int16))
+    # the fused forward + projection equals the two calls, in the graph too
+    assert torch.equal(out_f.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse_f.view(torch.int32), lse.view(torch.int32))
+    assert torch.equal(vout_f.view(torch.int16), vout_p.view(torch.int16))
 
 
 def test_prefill_step_graph():
