@@ -9,6 +9,8 @@
 //
 // Design (one workgroup of 4 waves per row, or per chunk of a row in the
 // split-KV pass; 64-key tiles):
+//  * the row's query (H x 576 bf16) is read from memory once per workgroup
+//    and handed to the waves through LDS, since each wave needs all of it;
 //  * the 64 records of a tile (64 x 656 B) are gathered with 16-byte loads
 //    into registers one tile ahead (4 threads per record), then stored to
 //    LDS as 64 consecutive records; the slot ids of the tile after that are
@@ -52,6 +54,11 @@ static_assert(4 * (kChunksPerThread - 1) + 1 == kChunks, "the last chunk belongs
 // (and with it O and the sum) is moved up.
 constexpr float kLazyRescale = 8.0f;
 constexpr int kLogitPitch = kTileKeys + 4;                                 // floats per head row
+// The row's query in LDS: bf16 per head row (576 + 8, so the 16 head rows
+// start 4 banks apart) and 16-byte pieces per head.
+constexpr int kQPitch = kQkDim + 8;
+constexpr int kQPieces = kQkDim / 8;
+constexpr int kQStage = (16 * kQPieces + kThreads - 1) / kThreads;  // pieces per thread
 
 typedef __attribute__((address_space(3))) intx2_t lds_intx2_t;
 
@@ -299,6 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   __shared__ __attribute__((aligned(16))) float s_logit[16 * kLogitPitch];
   __shared__ __attribute__((aligned(16))) float s_scale[4 * kTileKeys];
   __shared__ int s_slot[2][kTileKeys];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * kQPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,28 +321,47 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   u32x4_t qr[2];     // query, rope part
   u32x4_t qa[4][4];  // query, latent part: [tile][MFMA] bf16 A operands
   // The query is held as bf16 MFMA A operands (row = head n) for the whole
-  // row.  Loads are unconditional: a lane past the last head reads the last
-  // head's row and zeroes it.  rope part: lane (n, g) k-slots j of step st
-  // <-> rope d = 16g + 8st + j; latent tile b, MFMA m: k-slots j <-> dim
+  // row.  Every wave needs all of it, so the workgroup reads it from memory
+  // once: each thread loads kQStage 16-byte pieces (stage_query, issued early
+  // so that the first gather does not wait for it), they go to LDS with the
+  // first tile, and each wave reads its operands from there (finish_query).
+  // Heads past the last are zero.  rope part: lane (n, g) k-slots j of step
+  // st <-> rope d = 16g + 8st + j; latent tile b, MFMA m: k-slots j <-> dim
   // 128b + 64(m / 2) + 16g + 8(m % 2) + j.  The records' bytes are read
   // with the same mappings.
-  auto load_query = [&](int64_t t) {
-    const int nq = n < p.heads ? n : p.heads - 1;
-    const uint32_t qkeep = n < p.heads ? 0xFFFFFFFFu : 0u;
-    const uint16_t *qrow = p.q + t * p.q_st + (int64_t)nq * p.q_sh;
+  u32x4_t qst[kQStage];
+  auto stage_query = [&](int64_t t) {
+    const uint16_t *qbase = p.q + t * p.q_st;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + kLatent + 16 * g + 8 * st);
-      qr[st] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 128 * b + 64 * (m >> 1) + 16 * g + 8 * (m & 1));
-        qa[b][m] = u32x4_t{src[0] & qkeep, src[1] & qkeep, src[2] & qkeep, src[3] & qkeep};
+    for (int i = 0; i < kQStage; ++i) {
+      const int c = tid + kThreads * i;  // piece c % kQPieces of head c / kQPieces
+      const int hh = c / kQPieces;
+      if (hh < p.heads) {
+        const uint32_t *src =
+            reinterpret_cast<const uint32_t *>(qbase + (int64_t)hh * p.q_sh + 8 * (c - kQPieces * hh));
+        qst[i] = u32x4_t{src[0], src[1], src[2], src[3]};
+      } else {
+        qst[i] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto store_query = [&]() {  // before a barrier
+#pragma unroll
+    for (int i = 0; i < kQStage; ++i) {
+      const int c = tid + kThreads * i;
+      const int hh = c / kQPieces;
+      if (hh < 16) *reinterpret_cast<u32x4_t *>(s_q + hh * kQPitch + 8 * (c - kQPieces * hh)) = qst[i];
+    }
+  };
+  auto finish_query = [&]() {  // after that barrier
+    const uint16_t *qrow = s_q + n * kQPitch;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) qr[st] = *reinterpret_cast<const u32x4_t *>(qrow + kLatent + 16 * g + 8 * st);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        qa[b][m] = *reinterpret_cast<const u32x4_t *>(qrow + 128 * b + 64 * (m >> 1) + 16 * g + 8 * (m & 1));
   };
 
   // ---- this workgroup's entries: a whole row, or a chunk of one
@@ -363,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     }
     // the query after the ids: loads complete in order, so the first gather
     // waits for indptr and its slot id, not for the query
-    load_query(rr.t);
+    stage_query(rr.t);
     __builtin_amdgcn_sched_barrier(0);  // all of the above in flight before indptr is used
     clamp_range((int64_t)x0, (int64_t)x1, p.nnz, rr.beg, rr.lenp);
     int64_t lene = 0;
@@ -447,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     slot_t1 = fetch_entry(1, lane);
   }
   if (kSplit) {
-    load_query(t);  // after the slot ids, for the same reason
+    stage_query(t);  // after the slot ids, for the same reason
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -557,7 +584,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       s_slot[1][tid] = slot_of(slot_t1, 1, tid);
     }
     store_gather();  // tile 0
+    store_query();
     __syncthreads();
+    finish_query();
     if (ntiles > 1) issue_gather(1);
     for (int k = 0; k < ntiles; ++k) {
       const int buf = k & 1;
