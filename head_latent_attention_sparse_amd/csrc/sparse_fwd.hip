@@ -106,22 +106,23 @@ __device__ __forceinline__ void clamp_range(int64_t b, int64_t e, int64_t nnz, i
   len = e - b;
 }
 
-// ---- Split-KV plan, computed by every workgroup of the partial pass ----
-// The same plan in every workgroup (and no separate launch): row lengths
-// with the forward's clamping of indptr; a chunk size; each row's first
-// chunk (an exclusive prefix); then this workgroup's chunk.  The chunk size
-// is `forced` if given, otherwise the smallest of kPlanCandidates multiples
-// of 64 (at least kMinChunk) whose chunk total fits the `bound` workgroups,
-// so the partial pass is one round of the shortest chunks.  The candidates
-// run from ceil(n / bound) to ceil(n / (bound - rows)) (n = sum of lengths,
-// rows = the non-empty ones); the last always fits, since
+// ---- Split-KV plan, computed by every wave of the partial pass ----
+// Each wave computes the same plan on its own (no LDS, no barrier): row
+// lengths with the forward's clamping of indptr; a chunk size; each row's
+// first chunk (an exclusive prefix); then this workgroup's chunk.  The chunk
+// size is `forced` if given, otherwise the smallest of kPlanCandidates
+// multiples of 64 (at least kMinChunk) whose chunk total fits the `bound`
+// workgroups, so the partial pass is one round of the shortest chunks.  The
+// candidates run from ceil(n / bound) to ceil(n / (bound - rows)) (n = sum
+// of lengths, rows = the non-empty ones); the last always fits, since
 // sum ceil(len / C) <= n / C + rows.  Prefix values are capped at `bound`:
 // a non-monotone indptr (overlapping rows) loses chunks instead of indexing
-// out of range.  Thread i owns rows 2i and 2i + 1.
+// out of range.  Lane l owns rows l, l + 64, ... (at most kPlanRowsPerLane).
 constexpr int kMaxSplitRows = 512;
-constexpr int64_t kMinChunk = 512;
+constexpr int kPlanRowsPerLane = kMaxSplitRows / 64;
+constexpr uint32_t kMinChunk = 512;
+constexpr uint32_t kMaxChunk = 1u << 29;
 constexpr int kPlanCandidates = 4;
-static_assert(kMaxSplitRows == 2 * kThreads, "split plan: two rows per thread");
 
 // ceil(len / c) for 0 <= len < 2^29 and 64 <= c < 2^30: a float estimate
 // (off by at most 2) and an exact integer correction.
@@ -161,126 +162,115 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
 }
 __device__ __forceinline__ int32_t wave_sum(int32_t v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
-struct SplitPlanLds {
-  uint32_t n[4];  // per wave: sum of lengths (exact for non-decreasing CSR offsets: < 2^30)
-  int32_t rows[4];
-  int32_t cnt[kPlanCandidates][4];
-  int32_t wave_tot[4];
-  int32_t hit[6];  // row, chunk begin, row length, primary begin, primary length, extra begin
-};
-
 template <typename IdxT, bool kExtra>
-__device__ bool split_plan(const FwdKernelArgs &p, uint8_t *scratch, RowRange &rr) {
-  SplitPlanLds &sh = *reinterpret_cast<SplitPlanLds *>(scratch);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
+  const int lane = threadIdx.x & 63;
   const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
-  const int32_t tokens = p.tokens;
-  const int32_t r0 = 2 * tid;
+  const int32_t tokens = p.tokens;  // <= kMaxSplitRows
+  const int nj = (tokens + 63) >> 6;  // row slots in use per lane (uniform)
 
-  // rows r0 and r0 + 1: three offsets per segment, one round trip.
-  // len = the row's entries over both segments (< 2^30).
-  int32_t len[2] = {0, 0}, rb[2] = {0, 0}, lp[2] = {0, 0}, eb[2] = {0, 0};
-  if (r0 < tokens) {
-    const int r2 = r0 + 1 < tokens ? r0 + 2 : r0 + 1;
-    const IdxT x0 = indptr[r0], x1 = indptr[r0 + 1], x2 = indptr[r2];
-    IdxT y0 = 0, y1 = 0, y2 = 0;
-    if (kExtra) {
-      const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
-      y0 = eindptr[r0];
-      y1 = eindptr[r0 + 1];
-      y2 = eindptr[r2];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before any use
-    const int64_t xs[3] = {(int64_t)x0, (int64_t)x1, (int64_t)x2};
-    const int64_t ys[3] = {(int64_t)y0, (int64_t)y1, (int64_t)y2};
+  // this lane's rows: both segments' offsets, all requested at once
+  IdxT x0[kPlanRowsPerLane], x1[kPlanRowsPerLane], y0[kPlanRowsPerLane], y1[kPlanRowsPerLane];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int64_t b, l;
-      clamp_range(xs[i], xs[i + 1], p.nnz, b, l);
-      rb[i] = (int32_t)b;  // nnz < 2^29
-      lp[i] = (int32_t)l;
-      len[i] = (int32_t)l;
+  for (int j = 0; j < kPlanRowsPerLane; ++j) {
+    const int r = lane + 64 * j;
+    x0[j] = x1[j] = y0[j] = y1[j] = 0;
+    if (j < nj && r < tokens) {
+      x0[j] = indptr[r];
+      x1[j] = indptr[r + 1];
       if (kExtra) {
-        clamp_range(ys[i], ys[i + 1], p.ennz, b, l);
-        eb[i] = (int32_t)b;
-        len[i] += (int32_t)l;
+        const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
+        y0[j] = eindptr[r];
+        y1[j] = eindptr[r + 1];
       }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all loads in flight before any use
+  // len = the row's entries over both segments (< 2^30)
+  int32_t len[kPlanRowsPerLane], rb[kPlanRowsPerLane], lp[kPlanRowsPerLane], eb[kPlanRowsPerLane];
+#pragma unroll
+  for (int j = 0; j < kPlanRowsPerLane; ++j) {
+    int64_t b, l;
+    clamp_range((int64_t)x0[j], (int64_t)x1[j], p.nnz, b, l);
+    rb[j] = (int32_t)b;  // nnz < 2^29
+    lp[j] = (int32_t)l;
+    len[j] = (int32_t)l;
+    eb[j] = 0;
+    if (kExtra) {
+      clamp_range((int64_t)y0[j], (int64_t)y1[j], p.ennz, b, l);
+      eb[j] = (int32_t)b;
+      len[j] += (int32_t)l;
     }
   }
 
   int32_t chunk = p.forced_chunk;
   if (chunk <= 0) {
-    // For a malformed (decreasing) indptr the sums may wrap; every chunk size
-    // below is still in [kMinChunk, 2^29], and the caps keep chunks in range.
-    const int32_t nw = wave_sum(len[0] + len[1]);
-    const int32_t rw = wave_sum((len[0] > 0) + (len[1] > 0));
-    if (lane == 0) {
-      sh.n[wave] = (uint32_t)nw;
-      sh.rows[wave] = rw;
-    }
-    __syncthreads();
-    const int64_t n = (int64_t)(sh.n[0] + sh.n[1] + sh.n[2] + sh.n[3]);
-    const int64_t rows = sh.rows[0] + sh.rows[1] + sh.rows[2] + sh.rows[3];
-    const int64_t bound = p.bound;
-    const int64_t lo = max(kMinChunk, ((n + bound - 1) / bound + 63) & ~(int64_t)63);
-    const int64_t slack = bound > rows ? bound - rows : 1;
-    const int64_t hi = min(max(lo, ((n + slack - 1) / slack + 63) & ~(int64_t)63), (int64_t)1 << 29);
-    const int64_t step = max((int64_t)64, ((hi - lo) / (kPlanCandidates - 1) + 63) & ~(int64_t)63);
+    // For a malformed (overlapping) indptr n may wrap; every chunk size
+    // below is still in [kMinChunk, kMaxChunk], and the caps keep chunks in range.
+    int32_t nl = 0, rl = 0;
 #pragma unroll
-    for (int k = 0; k < kPlanCandidates; ++k) {
-      const int32_t c = (int32_t)min(lo + step * k, hi);
-      const float rcp = 1.0f / (float)c;
-      const int32_t cw = wave_sum(ceil_div_rcp(len[0], c, rcp) + ceil_div_rcp(len[1], c, rcp));
-      if (lane == 0) sh.cnt[k][wave] = cw;
+    for (int j = 0; j < kPlanRowsPerLane; ++j) {
+      if (j >= nj) break;
+      nl += len[j];
+      rl += len[j] > 0;
     }
-    __syncthreads();
+    const uint32_t n = (uint32_t)wave_sum(nl);
+    const uint32_t rows = (uint32_t)wave_sum(rl);
+    const uint32_t bound = (uint32_t)p.bound;  // the library's plan: a few times the compute units
+    auto cdiv = [](uint32_t a, uint32_t b) { return a / b + (a % b != 0u ? 1u : 0u); };
+    auto up64 = [](uint32_t x) { return (min(x, kMaxChunk) + 63u) & ~63u; };
+    const uint32_t lo = max(kMinChunk, up64(cdiv(n, bound)));
+    const uint32_t slack = bound > rows ? bound - rows : 1u;
+    const uint32_t hi = min(max(lo, up64(cdiv(n, slack))), kMaxChunk);
+    const uint32_t step = max(64u, up64((hi - lo) / (kPlanCandidates - 1)));
     chunk = (int32_t)hi;  // always fits
 #pragma unroll
-    for (int k = kPlanCandidates - 1; k >= 0; --k)
-      if (sh.cnt[k][0] + sh.cnt[k][1] + sh.cnt[k][2] + sh.cnt[k][3] <= bound) chunk = (int32_t)min(lo + step * k, hi);
-  }
-
-  // first chunk of each row: one block scan of this thread's two counts
-  const float rcp = 1.0f / (float)chunk;
-  const int32_t c0 = ceil_div_rcp(len[0], chunk, rcp), c1 = ceil_div_rcp(len[1], chunk, rcp);
-  const int32_t incl = wave_incl_scan(c0 + c1);
-  if (lane == 63) sh.wave_tot[wave] = incl;
-  __syncthreads();
-  int64_t first0 = incl - c0 - c1;
-  for (int w = 0; w < wave; ++w) first0 += sh.wave_tot[w];
-  const int64_t cap = p.bound;
-  const int64_t total = min((int64_t)sh.wave_tot[0] + sh.wave_tot[1] + sh.wave_tot[2] + sh.wave_tot[3], cap);
-  const int64_t f0 = min(first0, cap), f1 = min(first0 + c0, cap), f2 = min(first0 + c0 + c1, cap);
-  if (blockIdx.x == 0) {  // the merge reads the prefix
-    if (r0 < tokens) p.ws_prefix[r0] = (int32_t)f0;
-    if (r0 + 1 < tokens) p.ws_prefix[r0 + 1] = (int32_t)f1;
-    if (tid == 0) p.ws_prefix[tokens] = (int32_t)total;
-  }
-  const int64_t b = blockIdx.x;
+    for (int k = kPlanCandidates - 1; k >= 0; --k) {
+      const int32_t c = (int32_t)min(lo + step * k, hi);
+      const float rcp = 1.0f / (float)c;
+      int32_t cl = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t fb = i == 0 ? f0 : f1, fe = i == 0 ? f1 : f2;
-    if (r0 + i < tokens && fb <= b && b < fe) {
-      sh.hit[0] = r0 + i;
-      sh.hit[1] = (int32_t)(b - fb) * chunk;
-      sh.hit[2] = len[i];
-      sh.hit[3] = rb[i];
-      sh.hit[4] = lp[i];
-      sh.hit[5] = eb[i];
+      for (int j = 0; j < kPlanRowsPerLane; ++j) {
+        if (j >= nj) break;
+        cl += ceil_div_rcp(len[j], c, rcp);
+      }
+      if ((uint32_t)wave_sum(cl) <= bound) chunk = c;
     }
   }
-  __syncthreads();
-  const bool has_work = b < total;
-  if (has_work) {
-    rr.t = sh.hit[0];
-    rr.vb = sh.hit[1];
-    rr.ve = rr.vb + chunk < sh.hit[2] ? rr.vb + chunk : (int64_t)sh.hit[2];
-    rr.beg = sh.hit[3];
-    rr.lenp = sh.hit[4];
-    rr.ebeg = sh.hit[5];
+
+  // each row's first chunk (prefix in row order), capped at the bound; the
+  // row holding this workgroup's chunk; the merge's copy of the prefix
+  const float rcp = 1.0f / (float)chunk;
+  const int32_t cap = (int32_t)p.bound;
+  const int32_t b = (int32_t)blockIdx.x;
+  const bool writer = blockIdx.x == 0 && threadIdx.x < 64;
+  int32_t carry = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < kPlanRowsPerLane; ++j) {
+    if (j >= nj) break;
+    const int r = lane + 64 * j;
+    const int32_t c = ceil_div_rcp(len[j], chunk, rcp);  // 0 past the last row (len 0)
+    const int32_t incl = wave_incl_scan(c);
+    const int32_t f0 = min(carry + incl - c, cap), f1 = min(carry + incl, cap);
+    if (writer && r < tokens) p.ws_prefix[r] = f0;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(r < tokens && f0 <= b && b < f1);
+    if (hit != 0) {
+      const int src = (int)__builtin_ctzll(hit);
+      rr.t = __builtin_amdgcn_readlane(r, src);
+      // (unsigned: the product is only meaningful, and below 2^30, on the hit lane)
+      rr.vb = __builtin_amdgcn_readlane((int32_t)((uint32_t)(b - f0) * (uint32_t)chunk), src);
+      const int32_t rlen = __builtin_amdgcn_readlane(len[j], src);
+      rr.ve = rr.vb + chunk < rlen ? rr.vb + chunk : (int64_t)rlen;
+      rr.beg = __builtin_amdgcn_readlane(rb[j], src);
+      rr.lenp = __builtin_amdgcn_readlane(lp[j], src);
+      rr.ebeg = __builtin_amdgcn_readlane(eb[j], src);
+      found = true;
+    }
+    carry = min(carry + __builtin_amdgcn_readlane(incl, 63), cap);
   }
-  __syncthreads();  // the scratch (the tile buffer) is reused next
-  return has_work;
+  if (writer && lane == 0) p.ws_prefix[tokens] = carry;
+  return found && b < carry;
 }
 
 // QK^T partial of latent tile B for this lane's key: the float32 sum over
@@ -376,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   IdxT guess_id0 = 0, guess_t0 = 0, guess_t1 = 0;
   int64_t guess_beg = -1;
   if (kSplit) {
-    if (!split_plan<IdxT, kExtra>(p, s_rec, rr)) return;  // whole workgroup
+    if (!split_plan<IdxT, kExtra>(p, rr)) return;  // whole workgroup
   } else {
     const IdxT *indptr = static_cast<const IdxT *>(p.indptr);
     rr.t = blockIdx.x;
