@@ -110,12 +110,14 @@ __device__ __forceinline__ void clamp_range(int64_t b, int64_t e, int64_t nnz, i
 // Each wave computes the same plan on its own (no LDS, no barrier): row
 // lengths with the forward's clamping of indptr; a chunk size; each row's
 // first chunk (an exclusive prefix); then this workgroup's chunk.  The chunk
-// size is `forced` if given, otherwise the smallest of kPlanCandidates
+// size is `forced` if given, otherwise the smallest C of kPlanCandidates
 // multiples of 64 (at least kMinChunk) whose chunk total fits the `bound`
-// workgroups, so the partial pass is one round of the shortest chunks.  The
-// candidates run from ceil(n / bound) to ceil(n / (bound - rows)) (n = sum
-// of lengths, rows = the non-empty ones); the last always fits, since
-// sum ceil(len / C) <= n / C + rows.  Prefix values are capped at `bound`:
+// workgroups, so the partial pass is one round of the shortest chunks; then
+// C + kSkewEntries for the first half of the workgroups and C - kSkewEntries
+// for the rest, if that fits too.  The candidates run from ceil(n / bound)
+// to ceil(n / (bound - rows)) (n = sum of lengths, rows = the non-empty
+// ones); the last always fits, since sum ceil(len / C) <= n / C + rows.
+// Prefix values are capped at `bound`:
 // a non-monotone indptr (overlapping rows) loses chunks instead of indexing
 // out of range.  Lane l owns rows l, l + 64, ... (at most kPlanRowsPerLane).
 constexpr int kMaxSplitRows = 512;
@@ -162,6 +164,27 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
 }
 __device__ __forceinline__ int32_t wave_sum(int32_t v) { return __builtin_amdgcn_readlane(wave_incl_scan(v), 63); }
 
+constexpr int32_t kSkewEntries = 128;  // two tiles
+
+struct ChunkSizes {
+  int32_t ca, cb, na;
+  float rca, rcb;
+};
+__device__ __forceinline__ ChunkSizes chunk_sizes(int32_t ca, int32_t cb, int32_t na) {
+  return ChunkSizes{ca, cb, na, 1.0f / (float)ca, 1.0f / (float)cb};
+}
+// A row of len entries whose first chunk would be chunk pa if every chunk
+// had z.ca entries (pa: an exclusive prefix of ka = ceil(len / z.ca) over
+// the rows): its first na_row chunks (those below z.na) take z.ca entries
+// and the rest z.cb, k chunks in all.  Rows wholly below z.na keep their ka
+// chunks, the row across it is split there, the rows above use z.cb only.
+__device__ __forceinline__ void row_chunks(int32_t len, int32_t pa, int32_t ka, const ChunkSizes &z, int32_t &na_row,
+                                           int32_t &k) {
+  na_row = min(max(z.na - pa, 0), ka);
+  const int32_t rest = max(len - na_row * z.ca, 0);
+  k = na_row + ceil_div_rcp(rest, z.cb, z.rcb);
+}
+
 template <typename IdxT, bool kExtra>
 __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
   const int lane = threadIdx.x & 63;
@@ -203,10 +226,22 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
     }
   }
 
-  int32_t chunk = p.forced_chunk;
-  if (chunk <= 0) {
+  // Chunk sizes: the first z.na workgroups take chunks of z.ca entries, the
+  // others of z.cb.  Forced: one size.  Otherwise the first half of the
+  // bound (one workgroup per compute unit: workgroups are dispatched in
+  // index order, so these are the first on their unit) take chunks
+  // kSkewEntries longer than the base size and the second half
+  // kSkewEntries shorter: a compute unit's first workgroup gets its
+  // loads served ahead of its second, which would otherwise finish its
+  // equal share last, alone on the unit.  Which workgroup lands where only
+  // changes the speed, never the result.
+  ChunkSizes z;
+  if (p.forced_chunk > 0) {
+    z = chunk_sizes(p.forced_chunk, p.forced_chunk, 0);
+  } else {
     // For a malformed (overlapping) indptr n may wrap; every chunk size
-    // below is still in [kMinChunk, kMaxChunk], and the caps keep chunks in range.
+    // below is still in [kMinChunk - kSkewEntries, kMaxChunk + kSkewEntries],
+    // and the caps keep chunks in range.
     int32_t nl = 0, rl = 0;
 #pragma unroll
     for (int j = 0; j < kPlanRowsPerLane; ++j) {
@@ -216,57 +251,80 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
     }
     const uint32_t n = (uint32_t)wave_sum(nl);
     const uint32_t rows = (uint32_t)wave_sum(rl);
-    const uint32_t bound = (uint32_t)p.bound;  // the library's plan: a few times the compute units
+    const uint32_t bound = (uint32_t)p.bound;  // the library's plan: twice the compute units
     auto cdiv = [](uint32_t a, uint32_t b) { return a / b + (a % b != 0u ? 1u : 0u); };
     auto up64 = [](uint32_t x) { return (min(x, kMaxChunk) + 63u) & ~63u; };
     const uint32_t lo = max(kMinChunk, up64(cdiv(n, bound)));
     const uint32_t slack = bound > rows ? bound - rows : 1u;
     const uint32_t hi = min(max(lo, up64(cdiv(n, slack))), kMaxChunk);
     const uint32_t step = max(64u, up64((hi - lo) / (kPlanCandidates - 1)));
-    chunk = (int32_t)hi;  // always fits
+    int32_t c = (int32_t)hi;  // always fits
 #pragma unroll
     for (int k = kPlanCandidates - 1; k >= 0; --k) {
-      const int32_t c = (int32_t)min(lo + step * k, hi);
-      const float rcp = 1.0f / (float)c;
+      const int32_t ck = (int32_t)min(lo + step * k, hi);
+      const float rcp = 1.0f / (float)ck;
       int32_t cl = 0;
 #pragma unroll
       for (int j = 0; j < kPlanRowsPerLane; ++j) {
         if (j >= nj) break;
-        cl += ceil_div_rcp(len[j], c, rcp);
+        cl += ceil_div_rcp(len[j], ck, rcp);
       }
-      if ((uint32_t)wave_sum(cl) <= bound) chunk = c;
+      if ((uint32_t)wave_sum(cl) <= bound) c = ck;
     }
+    z = chunk_sizes(c, c, 0);
+    // the skewed sizes around the same base, where they fit too
+    const ChunkSizes y = chunk_sizes(c + kSkewEntries, c - kSkewEntries, (int32_t)(bound / 2));
+    int32_t carry_a = 0, kl = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanRowsPerLane; ++j) {
+      if (j >= nj) break;
+      const int32_t ka = ceil_div_rcp(len[j], y.ca, y.rca);
+      const int32_t inca = wave_incl_scan(ka);
+      int32_t na_row, kr;
+      row_chunks(len[j], carry_a + inca - ka, ka, y, na_row, kr);
+      kl += kr;
+      carry_a += __builtin_amdgcn_readlane(inca, 63);
+    }
+    if ((uint32_t)wave_sum(kl) <= bound) z = y;
   }
 
   // each row's first chunk (prefix in row order), capped at the bound; the
   // row holding this workgroup's chunk; the merge's copy of the prefix
-  const float rcp = 1.0f / (float)chunk;
   const int32_t cap = (int32_t)p.bound;
   const int32_t b = (int32_t)blockIdx.x;
   const bool writer = blockIdx.x == 0 && threadIdx.x < 64;
-  int32_t carry = 0;
+  int32_t carry = 0, carry_a = 0;
   bool found = false;
 #pragma unroll
   for (int j = 0; j < kPlanRowsPerLane; ++j) {
     if (j >= nj) break;
     const int r = lane + 64 * j;
-    const int32_t c = ceil_div_rcp(len[j], chunk, rcp);  // 0 past the last row (len 0)
+    const int32_t ka = ceil_div_rcp(len[j], z.ca, z.rca);  // 0 past the last row (len 0)
+    const int32_t inca = wave_incl_scan(ka);
+    int32_t na_row, c;
+    row_chunks(len[j], carry_a + inca - ka, ka, z, na_row, c);
     const int32_t incl = wave_incl_scan(c);
     const int32_t f0 = min(carry + incl - c, cap), f1 = min(carry + incl, cap);
     if (writer && r < tokens) p.ws_prefix[r] = f0;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(r < tokens && f0 <= b && b < f1);
     if (hit != 0) {
       const int src = (int)__builtin_ctzll(hit);
+      // chunk i of the row: na_row chunks of ca, then chunks of cb (unsigned:
+      // only meaningful, and below 2^30, on the hit lane)
+      const uint32_t i = (uint32_t)(b - f0), nar = (uint32_t)na_row;
+      const uint32_t start = i < nar ? i * (uint32_t)z.ca : nar * (uint32_t)z.ca + (i - nar) * (uint32_t)z.cb;
+      const uint32_t size = i < nar ? (uint32_t)z.ca : (uint32_t)z.cb;
       rr.t = __builtin_amdgcn_readlane(r, src);
-      // (unsigned: the product is only meaningful, and below 2^30, on the hit lane)
-      rr.vb = __builtin_amdgcn_readlane((int32_t)((uint32_t)(b - f0) * (uint32_t)chunk), src);
+      rr.vb = __builtin_amdgcn_readlane((int32_t)start, src);
+      const int32_t csize = __builtin_amdgcn_readlane((int32_t)size, src);
       const int32_t rlen = __builtin_amdgcn_readlane(len[j], src);
-      rr.ve = rr.vb + chunk < rlen ? rr.vb + chunk : (int64_t)rlen;
+      rr.ve = rr.vb + csize < rlen ? rr.vb + csize : (int64_t)rlen;
       rr.beg = __builtin_amdgcn_readlane(rb[j], src);
       rr.lenp = __builtin_amdgcn_readlane(lp[j], src);
       rr.ebeg = __builtin_amdgcn_readlane(eb[j], src);
       found = true;
     }
+    carry_a += __builtin_amdgcn_readlane(inca, 63);
     carry = min(carry + __builtin_amdgcn_readlane(incl, 63), cap);
   }
   if (writer && lane == 0) p.ws_prefix[tokens] = carry;
