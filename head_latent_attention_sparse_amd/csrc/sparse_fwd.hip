@@ -96,6 +96,7 @@ struct FwdKernelArgs {
 // the workgroup takes entries [vb, ve).
 struct RowRange {
   int64_t t, beg, lenp, ebeg, vb, ve;
+  int64_t chunk;  // split pass: the chunk's index in row order (its partial's slot)
 };
 
 // Clamp a CSR pair to [0, nnz] (a decreasing pair gives an empty range).
@@ -113,10 +114,11 @@ __device__ __forceinline__ void clamp_range(int64_t b, int64_t e, int64_t nnz, i
 // size is `forced` if given, otherwise the smallest C of kPlanCandidates
 // multiples of 64 (at least kMinChunk) whose chunk total fits the `bound`
 // workgroups, so the partial pass is one round of the shortest chunks; then
-// C + kSkewEntries for the first half of the workgroups and C - kSkewEntries
-// for the rest, if that fits too.  The candidates run from ceil(n / bound)
-// to ceil(n / (bound - rows)) (n = sum of lengths, rows = the non-empty
-// ones); the last always fits, since sum ceil(len / C) <= n / C + rows.
+// sizes alternating C + kSkewEntries, C - kSkewEntries along the chunk
+// order, if that fits too (the longer ones go to the first half of the
+// workgroups).  The candidates run from ceil(n / bound) to
+// ceil(n / (bound - rows)) (n = sum of lengths, rows = the non-empty ones);
+// the last always fits, since sum ceil(len / C) <= n / C + rows.
 // Prefix values are capped at `bound`:
 // a non-monotone indptr (overlapping rows) loses chunks instead of indexing
 // out of range.  Lane l owns rows l, l + 64, ... (at most kPlanRowsPerLane).
@@ -166,23 +168,35 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) { return __builtin_amdgcn
 
 constexpr int32_t kSkewEntries = 128;  // two tiles
 
-struct ChunkSizes {
-  int32_t ca, cb, na;
-  float rca, rcb;
-};
-__device__ __forceinline__ ChunkSizes chunk_sizes(int32_t ca, int32_t cb, int32_t na) {
-  return ChunkSizes{ca, cb, na, 1.0f / (float)ca, 1.0f / (float)cb};
+// Chunks of one row of len entries when chunk sizes alternate along the
+// chunk order: even chunks hold `big` entries, odd ones `small`
+// (big + small = c2, rcp2 = 1 / c2).  k0 / k1: the chunks it needs when its
+// first chunk is even / odd.  With big == small this is ceil(len / big).
+__device__ __forceinline__ void row_chunk_counts(int32_t len, int32_t big, int32_t small, float rcp2, int32_t &k0,
+                                                 int32_t &k1) {
+  const int32_t c2 = big + small;
+  const int32_t q = ceil_div_rcp(len + 1, c2, rcp2) - 1;  // floor(len / c2)
+  const int32_t rem = len - q * c2;
+  k0 = 2 * q + (rem == 0 ? 0 : (rem <= big ? 1 : 2));
+  k1 = 2 * q + (rem == 0 ? 0 : (rem <= small ? 1 : 2));
 }
-// A row of len entries whose first chunk would be chunk pa if every chunk
-// had z.ca entries (pa: an exclusive prefix of ka = ceil(len / z.ca) over
-// the rows): its first na_row chunks (those below z.na) take z.ca entries
-// and the rest z.cb, k chunks in all.  Rows wholly below z.na keep their ka
-// chunks, the row across it is split there, the rows above use z.cb only.
-__device__ __forceinline__ void row_chunks(int32_t len, int32_t pa, int32_t ka, const ChunkSizes &z, int32_t &na_row,
-                                           int32_t &k) {
-  na_row = min(max(z.na - pa, 0), ka);
-  const int32_t rest = max(len - na_row * z.ca, 0);
-  k = na_row + ceil_div_rcp(rest, z.cb, z.rcb);
+
+// Inclusive scan over the lanes (rows in order) of the maps "first chunk's
+// parity p -> chunks of the rows so far": a lane holds (a0, a1) = its row's
+// (k0, k1) and ends with the composition of lanes 0..lane, which is
+// associative: (left then self)(p) = left(p) + self((p + left(p)) & 1).
+__device__ __forceinline__ void wave_scan_parity(int32_t &a0, int32_t &a1) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t l0 = __shfl_up(a0, d, 64), l1 = __shfl_up(a1, d, 64);
+    if (lane >= d) {
+      const int32_t n0 = l0 + ((l0 & 1) ? a1 : a0);
+      const int32_t n1 = l1 + ((l1 & 1) ? a0 : a1);
+      a0 = n0;
+      a1 = n1;
+    }
+  }
 }
 
 template <typename IdxT, bool kExtra>
@@ -226,19 +240,18 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
     }
   }
 
-  // Chunk sizes: the first z.na workgroups take chunks of z.ca entries, the
-  // others of z.cb.  Forced: one size.  Otherwise the first half of the
-  // bound (one workgroup per compute unit: workgroups are dispatched in
-  // index order, so these are the first on their unit) take chunks
-  // kSkewEntries longer than the base size and the second half
-  // kSkewEntries shorter: a compute unit's first workgroup gets its
-  // loads served ahead of its second, which would otherwise finish its
-  // equal share last, alone on the unit.  Which workgroup lands where only
-  // changes the speed, never the result.
-  ChunkSizes z;
-  if (p.forced_chunk > 0) {
-    z = chunk_sizes(p.forced_chunk, p.forced_chunk, 0);
-  } else {
+  // Chunk sizes: even chunks (in row order) hold `big` entries, odd ones
+  // `small`.  Forced: one size.  Otherwise `big` = C + kSkewEntries and
+  // `small` = C - kSkewEntries when that fits the bound too, else both C.
+  // Even chunk 2i goes to workgroup i and odd chunk 2i + 1 to workgroup
+  // W / 2 + i: workgroups are dispatched in index order, one per compute
+  // unit first, and a unit's first workgroup gets its loads served ahead
+  // of its second, which with equal chunks finishes last, alone on the
+  // unit.  Where a workgroup lands only changes the speed: the chunks, and
+  // so the results, depend on indptr and the bound alone.
+  const int32_t cap = (int32_t)p.bound;
+  int32_t big = p.forced_chunk, small = p.forced_chunk;
+  if (p.forced_chunk <= 0) {
     // For a malformed (overlapping) indptr n may wrap; every chunk size
     // below is still in [kMinChunk - kSkewEntries, kMaxChunk + kSkewEntries],
     // and the caps keep chunks in range.
@@ -271,49 +284,59 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
       }
       if ((uint32_t)wave_sum(cl) <= bound) c = ck;
     }
-    z = chunk_sizes(c, c, 0);
-    // the skewed sizes around the same base, where they fit too
-    const ChunkSizes y = chunk_sizes(c + kSkewEntries, c - kSkewEntries, (int32_t)(bound / 2));
-    int32_t carry_a = 0, kl = 0;
+    big = small = c;
+    if ((bound & 1u) == 0u) {  // the alternating sizes around the same C, where they fit too
+      const int32_t b2 = c + kSkewEntries, s2 = c - kSkewEntries;
+      const float rcp2 = 1.0f / (float)(b2 + s2);
+      int32_t f = 0;
 #pragma unroll
-    for (int j = 0; j < kPlanRowsPerLane; ++j) {
-      if (j >= nj) break;
-      const int32_t ka = ceil_div_rcp(len[j], y.ca, y.rca);
-      const int32_t inca = wave_incl_scan(ka);
-      int32_t na_row, kr;
-      row_chunks(len[j], carry_a + inca - ka, ka, y, na_row, kr);
-      kl += kr;
-      carry_a += __builtin_amdgcn_readlane(inca, 63);
+      for (int j = 0; j < kPlanRowsPerLane; ++j) {
+        if (j >= nj) break;
+        int32_t a0, a1;
+        row_chunk_counts(len[j], b2, s2, rcp2, a0, a1);
+        wave_scan_parity(a0, a1);
+        f += __builtin_amdgcn_readlane((f & 1) ? a1 : a0, 63);
+      }
+      if ((uint32_t)f <= bound) {
+        big = b2;
+        small = s2;
+      }
     }
-    if ((uint32_t)wave_sum(kl) <= bound) z = y;
   }
 
-  // each row's first chunk (prefix in row order), capped at the bound; the
-  // row holding this workgroup's chunk; the merge's copy of the prefix
-  const int32_t cap = (int32_t)p.bound;
+  // This workgroup's chunk index; each row's first chunk (a prefix in row
+  // order, in which a row's chunk count depends on the parity of its first
+  // chunk), capped at the bound; the row holding this workgroup's chunk;
+  // the merge's copy of the prefix.
   const int32_t b = (int32_t)blockIdx.x;
+  const int32_t jc = big == small ? b : (b < cap / 2 ? 2 * b : 2 * (b - cap / 2) + 1);
+  const float rcp2 = 1.0f / (float)(big + small);
   const bool writer = blockIdx.x == 0 && threadIdx.x < 64;
-  int32_t carry = 0, carry_a = 0;
+  int32_t carry = 0;  // chunks of the rows so far (uncapped: its parity matters)
   bool found = false;
 #pragma unroll
   for (int j = 0; j < kPlanRowsPerLane; ++j) {
     if (j >= nj) break;
     const int r = lane + 64 * j;
-    const int32_t ka = ceil_div_rcp(len[j], z.ca, z.rca);  // 0 past the last row (len 0)
-    const int32_t inca = wave_incl_scan(ka);
-    int32_t na_row, c;
-    row_chunks(len[j], carry_a + inca - ka, ka, z, na_row, c);
-    const int32_t incl = wave_incl_scan(c);
-    const int32_t f0 = min(carry + incl - c, cap), f1 = min(carry + incl, cap);
+    int32_t k0, k1;  // 0 past the last row (len 0)
+    row_chunk_counts(len[j], big, small, rcp2, k0, k1);
+    int32_t a0 = k0, a1 = k1;
+    wave_scan_parity(a0, a1);
+    int32_t e0 = __shfl_up(a0, 1, 64), e1 = __shfl_up(a1, 1, 64);  // the rows before this lane's
+    if (lane == 0) e0 = e1 = 0;
+    const int32_t fr = carry + ((carry & 1) ? e1 : e0);
+    const int32_t kr = (fr & 1) ? k1 : k0;
+    const int32_t f0 = min(fr, cap), f1 = min(fr + kr, cap);
     if (writer && r < tokens) p.ws_prefix[r] = f0;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(r < tokens && f0 <= b && b < f1);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(r < tokens && f0 <= jc && jc < f1);
     if (hit != 0) {
       const int src = (int)__builtin_ctzll(hit);
-      // chunk i of the row: na_row chunks of ca, then chunks of cb (unsigned:
-      // only meaningful, and below 2^30, on the hit lane)
-      const uint32_t i = (uint32_t)(b - f0), nar = (uint32_t)na_row;
-      const uint32_t start = i < nar ? i * (uint32_t)z.ca : nar * (uint32_t)z.ca + (i - nar) * (uint32_t)z.cb;
-      const uint32_t size = i < nar ? (uint32_t)z.ca : (uint32_t)z.cb;
+      // chunk i of the row starts after e even and i - e odd chunks
+      // (unsigned: only meaningful, and below 2^30, on the hit lane)
+      const uint32_t fu = (uint32_t)fr, i = (uint32_t)(jc - fr);
+      const uint32_t e = ((fu + i + 1u) >> 1) - ((fu + 1u) >> 1);
+      const uint32_t start = e * (uint32_t)big + (i - e) * (uint32_t)small;
+      const uint32_t size = ((fu + i) & 1u) ? (uint32_t)small : (uint32_t)big;
       rr.t = __builtin_amdgcn_readlane(r, src);
       rr.vb = __builtin_amdgcn_readlane((int32_t)start, src);
       const int32_t csize = __builtin_amdgcn_readlane((int32_t)size, src);
@@ -322,13 +345,14 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
       rr.beg = __builtin_amdgcn_readlane(rb[j], src);
       rr.lenp = __builtin_amdgcn_readlane(lp[j], src);
       rr.ebeg = __builtin_amdgcn_readlane(eb[j], src);
+      rr.chunk = jc;
       found = true;
     }
-    carry_a += __builtin_amdgcn_readlane(inca, 63);
-    carry = min(carry + __builtin_amdgcn_readlane(incl, 63), cap);
+    carry += __builtin_amdgcn_readlane((carry & 1) ? a1 : a0, 63);
   }
-  if (writer && lane == 0) p.ws_prefix[tokens] = carry;
-  return found && b < carry;
+  const int32_t total = min(carry, cap);
+  if (writer && lane == 0) p.ws_prefix[tokens] = total;
+  return found && jc < total;
 }
 
 // QK^T partial of latent tile B for this lane's key: the float32 sum over
@@ -683,7 +707,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       if (kLse && wave == 0 && g == 0)
         p.lse[t * p.heads + n] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
     } else {
-      const int64_t row = (int64_t)blockIdx.x * p.heads + n;  // chunk id * H + head
+      const int64_t row = rr.chunk * p.heads + n;  // chunk index * H + head
       float *wo = p.ws_out + row * kLatent + 128 * wave + 4 * g;
 #pragma unroll
       for (int m = 0; m < 8; ++m) *reinterpret_cast<floatx4_t *>(wo + 16 * m) = oacc[m] * inv;
