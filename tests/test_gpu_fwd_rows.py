@@ -3,7 +3,8 @@ rows (bar as for the forward).  Without split: more rows than the chip
 holds workgroups at once, with empty rows, rows of 1 and 2 key tiles,
 tile-aligned and ragged long rows, and a long row that is all masked,
 interleaved with a period coprime to any power-of-two grid.  With split:
-row counts that take each shape of the partial merge."""
+row counts that take each shape of the partial merge, and 130 long rows
+whose chunks take the alternating sizes across the plan's 64-row slots."""
 
 import numpy as np
 import pytest
@@ -163,3 +164,61 @@ def test_split_without_lse(t, with_sink):
     assert lse is None
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE, sink=sink)
     assert_fwd_close(out, None, ref_out, ref_lse, f"split without lse T={t}")
+
+
+def _alternating_chunk_total(lens, bound, skew=128):
+    """The split plan's rule, restated to choose inputs that reach it: the
+    smallest of four candidate sizes C whose ceil-chunk total fits the bound,
+    then sizes alternating C + skew, C - skew along the chunk order, a row's
+    count depending on the parity of its first chunk.  Returns (C, total of
+    the alternating plan, the rows' first-chunk parities)."""
+    up64 = lambda x: (min(x, 1 << 29) + 63) // 64 * 64
+    cdiv = lambda a, b: -(-a // b)
+    n, rows = int(sum(lens)), int(sum(1 for x in lens if x > 0))
+    lo = max(512, up64(cdiv(n, bound)))
+    hi = min(max(lo, up64(cdiv(n, bound - rows if bound > rows else 1))), 1 << 29)
+    step = max(64, up64((hi - lo) // 3))
+    c = hi
+    for k in range(3, -1, -1):
+        ck = min(lo + step * k, hi)
+        if sum(cdiv(int(x), ck) for x in lens) <= bound:
+            c = ck
+    big, small, f, parities = c + skew, c - skew, 0, []
+    for x in lens:
+        x = int(x)
+        q, rem = divmod(x, big + small)
+        first = big if f % 2 == 0 else small
+        parities.append(f % 2)
+        f += 2 * q + (0 if rem == 0 else (1 if rem <= first else 2))
+    return c, f, parities
+
+
+def test_split_many_rows_alternating_chunks():
+    """130 split rows (three 64-row slots of the plan's scans) of 3000-9000
+    entries, where the alternating chunk sizes fit the bound: rows start on
+    even and odd chunks across the slots, so the parity carried between
+    slots decides every later row's chunks.  One row empty, one all masked,
+    10% of entries masked; all rows against the oracle."""
+    t = 130
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator().manual_seed(61)
+    n = 8192
+    q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
+    lens = torch.randint(3000, 9001, (t,), generator=g).numpy().astype(np.int64)
+    lens[70] = 0
+    ptr = np.concatenate([[0], np.cumsum(lens)])
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g).numpy().astype(np.int64)
+    idx[torch.rand(int(ptr[-1]), generator=g).numpy() < 0.1] = -1
+    idx[ptr[100]:ptr[101]] = -1
+    bound = mla.split_workgroups(t, idx.size, cus)
+    assert bound > 0
+    c, total, parities = _alternating_chunk_total(lens, bound)
+    assert total <= bound, "the alternating sizes must fit for this test to reach them"
+    assert 0 < sum(parities[64:]) < t - 64, "later slots must hold rows starting on both parities"
+    say(f"split T={t}, bound {bound}: base chunk {c}, {total} alternating chunks")
+    out, lse = run(q, rec, ptr, idx, torch.int32)
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
+    assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t} alternating chunks")
