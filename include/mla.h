@@ -81,9 +81,9 @@ typedef enum mla_status {
  *     lse[t,h]   = ln sum_j exp(z_j)           (float32, natural log).
  * A row with no such entry gives out = 0 and lse = -inf.  A slot listed
  * twice counts twice.  When there are too few rows to fill the GPU (and at
- * most 512), each row's entries are cut into fixed-size chunks (split-KV):
- * every workgroup of a partial pass plans the chunks from indptr on the
- * device and computes one chunk's float32 partial and LSE, and a second
+ * most 512), each row's entries are cut into chunks (split-KV): every
+ * workgroup of a partial pass plans the chunks from indptr on the device
+ * and computes one chunk's float32 partial and LSE, and a second
  * launch combines each row's partials by their LSEs (the merge named by
  * merge_attn_states on the kimi_k3 nvidia mla page).
  *
@@ -235,8 +235,11 @@ mla_status_t mla_sparse_fwd_v_up_proj(const void *q, int64_t num_tokens, int32_t
  * bounds known on the host, as the split counts of the decode cores on the
  * kimi_k3 specialized-decode page are (PreparedMla.fill_splits / max_seq).
  * Without a forced chunk the chunk size is then picked on the device from
- * the actual row lengths: the smallest multiple of 64 entries (at least 512)
- * whose chunks fit that many workgroups.  Returns -1 for invalid arguments
+ * the actual row lengths: the smallest multiple C of 64 entries (at least
+ * 512) whose chunks fit that many workgroups, then, where they fit too,
+ * sizes alternating C + 128 and C - 128 along the chunk order.  The chunks
+ * depend on indptr and this count alone, so results are reproducible.
+ * Returns -1 for invalid arguments
  * (negative sizes, num_tokens >= 2^31 - 1 or num_indices >= 2^29, the
  * forward's own limits, or unknown flag bits).
  */
