@@ -185,19 +185,26 @@ __device__ __forceinline__ void row_chunk_counts(int32_t len, int32_t big, int32
 // parity p -> chunks of the rows so far": a lane holds (a0, a1) = its row's
 // (k0, k1) and ends with the composition of lanes 0..lane, which is
 // associative: (left then self)(p) = left(p) + self((p + left(p)) & 1).
-__device__ __forceinline__ void wave_scan_parity(int32_t &a0, int32_t &a1) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t l0 = __shfl_up(a0, d, 64), l1 = __shfl_up(a1, d, 64);
-    if (lane >= d) {
-      const int32_t n0 = l0 + ((l0 & 1) ? a1 : a0);
-      const int32_t n1 = l1 + ((l1 & 1) ? a0 : a1);
-      a0 = n0;
-      a1 = n1;
-    }
-  }
+// The same DPP network as wave_incl_scan; a lane without a source reads
+// (0, 0), the identity map.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void parity_step(int32_t &a0, int32_t &a1) {
+  const int32_t l0 = dpp_i32<kCtrl, kRowMask>(a0), l1 = dpp_i32<kCtrl, kRowMask>(a1);
+  const int32_t n0 = l0 + ((l0 & 1) ? a1 : a0);
+  const int32_t n1 = l1 + ((l1 & 1) ? a0 : a1);
+  a0 = n0;
+  a1 = n1;
 }
+__device__ __forceinline__ void wave_scan_parity(int32_t &a0, int32_t &a1) {
+  parity_step<0x111, 0xf>(a0, a1);  // row_shr:1
+  parity_step<0x112, 0xf>(a0, a1);  // row_shr:2
+  parity_step<0x114, 0xf>(a0, a1);  // row_shr:4
+  parity_step<0x118, 0xf>(a0, a1);  // row_shr:8
+  parity_step<0x142, 0xa>(a0, a1);  // row_bcast:15 into rows 1 and 3
+  parity_step<0x143, 0xc>(a0, a1);  // row_bcast:31 into rows 2 and 3
+}
+// The value of the lane below (0 for lane 0): DPP wave_shr:1.
+__device__ __forceinline__ int32_t lane_below(int32_t v) { return dpp_i32<0x138, 0xf>(v); }
 
 template <typename IdxT, bool kExtra>
 __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
@@ -250,7 +257,26 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
   // unit.  Where a workgroup lands only changes the speed: the chunks, and
   // so the results, depend on indptr and the bound alone.
   const int32_t cap = (int32_t)p.bound;
+  // Per row slot: the row's chunk counts (k0, k1) and their parity scan, for
+  // the sizes in use; returns all rows' chunks (uncapped).
+  int32_t K0[kPlanRowsPerLane], K1[kPlanRowsPerLane], S0[kPlanRowsPerLane], S1[kPlanRowsPerLane];
+  auto scan_rows = [&](int32_t bg, int32_t sm) {
+    const float rcp2 = 1.0f / (float)(bg + sm);
+    int32_t f = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanRowsPerLane; ++j) {
+      K0[j] = K1[j] = S0[j] = S1[j] = 0;
+      if (j >= nj) continue;
+      row_chunk_counts(len[j], bg, sm, rcp2, K0[j], K1[j]);
+      S0[j] = K0[j];
+      S1[j] = K1[j];
+      wave_scan_parity(S0[j], S1[j]);
+      f += __builtin_amdgcn_readlane((f & 1) ? S1[j] : S0[j], 63);
+    }
+    return f;
+  };
   int32_t big = p.forced_chunk, small = p.forced_chunk;
+  bool scanned = false;
   if (p.forced_chunk <= 0) {
     // For a malformed (overlapping) indptr n may wrap; every chunk size
     // below is still in [kMinChunk - kSkewEntries, kMaxChunk + kSkewEntries],
@@ -285,24 +311,14 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
       if ((uint32_t)wave_sum(cl) <= bound) c = ck;
     }
     big = small = c;
-    if ((bound & 1u) == 0u) {  // the alternating sizes around the same C, where they fit too
-      const int32_t b2 = c + kSkewEntries, s2 = c - kSkewEntries;
-      const float rcp2 = 1.0f / (float)(b2 + s2);
-      int32_t f = 0;
-#pragma unroll
-      for (int j = 0; j < kPlanRowsPerLane; ++j) {
-        if (j >= nj) break;
-        int32_t a0, a1;
-        row_chunk_counts(len[j], b2, s2, rcp2, a0, a1);
-        wave_scan_parity(a0, a1);
-        f += __builtin_amdgcn_readlane((f & 1) ? a1 : a0, 63);
-      }
-      if ((uint32_t)f <= bound) {
-        big = b2;
-        small = s2;
-      }
+    // the alternating sizes around the same C, where they fit too
+    if ((bound & 1u) == 0u && (uint32_t)scan_rows(c + kSkewEntries, c - kSkewEntries) <= bound) {
+      big = c + kSkewEntries;
+      small = c - kSkewEntries;
+      scanned = true;
     }
   }
+  if (!scanned) scan_rows(big, small);
 
   // This workgroup's chunk index; each row's first chunk (a prefix in row
   // order, in which a row's chunk count depends on the parity of its first
@@ -310,7 +326,6 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
   // the merge's copy of the prefix.
   const int32_t b = (int32_t)blockIdx.x;
   const int32_t jc = big == small ? b : (b < cap / 2 ? 2 * b : 2 * (b - cap / 2) + 1);
-  const float rcp2 = 1.0f / (float)(big + small);
   const bool writer = blockIdx.x == 0 && threadIdx.x < 64;
   int32_t carry = 0;  // chunks of the rows so far (uncapped: its parity matters)
   bool found = false;
@@ -318,14 +333,9 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
   for (int j = 0; j < kPlanRowsPerLane; ++j) {
     if (j >= nj) break;
     const int r = lane + 64 * j;
-    int32_t k0, k1;  // 0 past the last row (len 0)
-    row_chunk_counts(len[j], big, small, rcp2, k0, k1);
-    int32_t a0 = k0, a1 = k1;
-    wave_scan_parity(a0, a1);
-    int32_t e0 = __shfl_up(a0, 1, 64), e1 = __shfl_up(a1, 1, 64);  // the rows before this lane's
-    if (lane == 0) e0 = e1 = 0;
+    const int32_t e0 = lane_below(S0[j]), e1 = lane_below(S1[j]);  // the rows before this lane's
     const int32_t fr = carry + ((carry & 1) ? e1 : e0);
-    const int32_t kr = (fr & 1) ? k1 : k0;
+    const int32_t kr = (fr & 1) ? K1[j] : K0[j];  // 0 past the last row (len 0)
     const int32_t f0 = min(fr, cap), f1 = min(fr + kr, cap);
     if (writer && r < tokens) p.ws_prefix[r] = f0;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(r < tokens && f0 <= jc && jc < f1);
@@ -348,7 +358,7 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
       rr.chunk = jc;
       found = true;
     }
-    carry += __builtin_amdgcn_readlane((carry & 1) ? a1 : a0, 63);
+    carry += __builtin_amdgcn_readlane((carry & 1) ? S1[j] : S0[j], 63);
   }
   const int32_t total = min(carry, cap);
   if (writer && lane == 0) p.ws_prefix[tokens] = total;
