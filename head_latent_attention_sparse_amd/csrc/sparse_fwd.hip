@@ -213,20 +213,21 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
   const int32_t tokens = p.tokens;  // <= kMaxSplitRows
   const int nj = (tokens + 63) >> 6;  // row slots in use per lane (uniform)
 
-  // this lane's rows: both segments' offsets, all requested at once
+  // this lane's rows: both segments' offsets, all requested at once and
+  // unconditionally (a slot past the last row reads indptr[T] twice: an
+  // empty row), so no load waits on another
   IdxT x0[kPlanRowsPerLane], x1[kPlanRowsPerLane], y0[kPlanRowsPerLane], y1[kPlanRowsPerLane];
 #pragma unroll
   for (int j = 0; j < kPlanRowsPerLane; ++j) {
-    const int r = lane + 64 * j;
-    x0[j] = x1[j] = y0[j] = y1[j] = 0;
-    if (j < nj && r < tokens) {
-      x0[j] = indptr[r];
-      x1[j] = indptr[r + 1];
-      if (kExtra) {
-        const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
-        y0[j] = eindptr[r];
-        y1[j] = eindptr[r + 1];
-      }
+    const int r = lane + 64 * j < tokens ? lane + 64 * j : tokens;
+    const int r1 = r < tokens ? r + 1 : tokens;
+    x0[j] = indptr[r];
+    x1[j] = indptr[r1];
+    y0[j] = y1[j] = 0;
+    if (kExtra) {
+      const IdxT *eindptr = static_cast<const IdxT *>(p.eindptr);
+      y0[j] = eindptr[r];
+      y1[j] = eindptr[r1];
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // all loads in flight before any use
@@ -412,19 +413,19 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
   // 128b + 64(m / 2) + 16g + 8(m % 2) + j.  The records' bytes are read
   // with the same mappings.
   u32x4_t qst[kQStage];
+  // The loads are unconditional (a piece past the last head reads the last
+  // head's first piece and is zeroed when stored), so a later wait on the
+  // slot ids counts them and does not wait for them.
   auto stage_query = [&](int64_t t) {
     const uint16_t *qbase = p.q + t * p.q_st;
 #pragma unroll
     for (int i = 0; i < kQStage; ++i) {
       const int c = tid + kThreads * i;  // piece c % kQPieces of head c / kQPieces
       const int hh = c / kQPieces;
-      if (hh < p.heads) {
-        const uint32_t *src =
-            reinterpret_cast<const uint32_t *>(qbase + (int64_t)hh * p.q_sh + 8 * (c - kQPieces * hh));
-        qst[i] = u32x4_t{src[0], src[1], src[2], src[3]};
-      } else {
-        qst[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      const bool in = hh < p.heads;  // else piece 0 of the last head, in bounds
+      const int hc = in ? hh : p.heads - 1, pc = in ? c - kQPieces * hh : 0;
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(qbase + (int64_t)hc * p.q_sh + 8 * pc);
+      qst[i] = u32x4_t{src[0], src[1], src[2], src[3]};
     }
   };
   auto store_query = [&]() {  // before a barrier
@@ -432,7 +433,11 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
     for (int i = 0; i < kQStage; ++i) {
       const int c = tid + kThreads * i;
       const int hh = c / kQPieces;
-      if (hh < 16) *reinterpret_cast<u32x4_t *>(s_q + hh * kQPitch + 8 * (c - kQPieces * hh)) = qst[i];
+      const uint32_t keep = hh < p.heads ? 0xFFFFFFFFu : 0u;
+      const u32x4_t v = qst[i];
+      if (hh < 16)
+        *reinterpret_cast<u32x4_t *>(s_q + hh * kQPitch + 8 * (c - kQPieces * hh)) =
+            u32x4_t{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
     }
   };
   auto finish_query = [&]() {  // after that barrier
