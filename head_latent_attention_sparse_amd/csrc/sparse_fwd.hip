@@ -128,8 +128,9 @@ constexpr uint32_t kMinChunk = 512;
 constexpr uint32_t kMaxChunk = 1u << 29;
 constexpr int kPlanCandidates = 4;
 
-// ceil(len / c) for 0 <= len < 2^29 and 64 <= c < 2^30: a float estimate
-// (off by at most 2) and an exact integer correction.
+// ceil(len / c) for 0 <= len <= 2^30 and 64 <= c <= 2^30 (rcp = 1 / c): a
+// float estimate (off by at most 2: len / c < 2^24 and the estimate's
+// relative error is below 2^-23) and an exact integer correction.
 __device__ __forceinline__ int32_t ceil_div_rcp(int32_t len, int32_t c, float rcp) {
   int32_t q = (int32_t)((float)len * rcp);
   int32_t r = len - q * c;
