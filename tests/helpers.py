@@ -132,3 +132,67 @@ def assert_fwd_close(out, lse, ref_out, ref_lse, what=""):
         assert np.all(np.isfinite(l[fin])), f"{what}: non-finite lse"
         d = np.abs(l[fin] - ref_lse[fin])
         assert d.size == 0 or d.max() <= LSE_ATOL, f"{what}: lse off by {d.max()}"
+
+
+# ---- The split plan's chunking rule, restated for tests (the kernel's
+# split_plan computes it on the device).  Candidate sizes C are multiples of
+# 64 between ceil(n / W) and ceil(n / (W - rows)), at least 512; the smallest
+# whose chunk total fits W workgroups is kept; then chunk sizes alternate
+# C + 128, C - 128 along the chunk order if that fits W too.  With two sizes a
+# row's chunk count depends on the parity of its first chunk.
+SKEW_ENTRIES = 128
+
+
+def plan_row_counts(length, big, small):
+    """Chunks of a row of `length` entries when its first chunk is even (big
+    first) and when it is odd (small first)."""
+    q, rem = divmod(int(length), big + small)
+    k0 = 2 * q + (0 if rem == 0 else (1 if rem <= big else 2))
+    k1 = 2 * q + (0 if rem == 0 else (1 if rem <= small else 2))
+    return k0, k1
+
+
+def plan_chunk_sizes(lens, bound):
+    """(big, small): the chunk sizes the plan picks for these row lengths."""
+    up64 = lambda x: (min(x, 1 << 29) + 63) // 64 * 64
+    cdiv = lambda a, b: -(-a // b)
+    n, rows = int(sum(lens)), int(sum(1 for x in lens if x > 0))
+    lo = max(512, up64(cdiv(n, bound)))
+    hi = min(max(lo, up64(cdiv(n, bound - rows if bound > rows else 1))), 1 << 29)
+    step = max(64, up64((hi - lo) // 3))
+    c = hi
+    for k in range(3, -1, -1):
+        ck = min(lo + step * k, hi)
+        if sum(cdiv(int(x), ck) for x in lens) <= bound:
+            c = ck
+    big, small = c + SKEW_ENTRIES, c - SKEW_ENTRIES
+    if bound % 2 == 0 and plan_first_chunks(lens, big, small)[-1] <= bound:
+        return big, small
+    return c, c
+
+
+def plan_first_chunks(lens, big, small):
+    """Each row's first chunk index and, last, the total: a prefix in row
+    order, each row's count taken at the parity of its first chunk."""
+    f = [0]
+    for x in lens:
+        k0, k1 = plan_row_counts(x, big, small)
+        f.append(f[-1] + (k1 if f[-1] % 2 else k0))
+    return f
+
+
+def plan_chunk_of_workgroup(b, bound, big, small):
+    """The chunk index workgroup b takes: even chunks go to the first half of
+    the workgroups (longer chunks), odd ones to the second."""
+    if big == small:
+        return b
+    half = bound // 2
+    return 2 * b if b < half else 2 * (b - half) + 1
+
+
+def plan_chunk_range(f_row, i, big, small):
+    """[start, start + size) of chunk i of a row whose first chunk is f_row
+    (before clipping to the row's length)."""
+    even_before = (f_row + i + 1) // 2 - (f_row + 1) // 2
+    start = even_before * big + (i - even_before) * small
+    return start, (big if (f_row + i) % 2 == 0 else small)

@@ -13,7 +13,7 @@ import torch
 import head_latent_attention_sparse_amd as mla
 from oracle import encode_records, sparse_fwd as oracle_fwd
 from head_latent_attention_sparse_amd.workloads import bf16_bits
-from tests.helpers import assert_fwd_close, say
+from tests.helpers import assert_fwd_close, plan_chunk_sizes, plan_first_chunks, say
 
 pytestmark = pytest.mark.gpu
 
@@ -166,39 +166,13 @@ def test_split_without_lse(t, with_sink):
     assert_fwd_close(out, None, ref_out, ref_lse, f"split without lse T={t}")
 
 
-def _alternating_chunk_total(lens, bound, skew=128):
-    """The split plan's rule, restated to choose inputs that reach it: the
-    smallest of four candidate sizes C whose ceil-chunk total fits the bound,
-    then sizes alternating C + skew, C - skew along the chunk order, a row's
-    count depending on the parity of its first chunk.  Returns (C, total of
-    the alternating plan, the rows' first-chunk parities)."""
-    up64 = lambda x: (min(x, 1 << 29) + 63) // 64 * 64
-    cdiv = lambda a, b: -(-a // b)
-    n, rows = int(sum(lens)), int(sum(1 for x in lens if x > 0))
-    lo = max(512, up64(cdiv(n, bound)))
-    hi = min(max(lo, up64(cdiv(n, bound - rows if bound > rows else 1))), 1 << 29)
-    step = max(64, up64((hi - lo) // 3))
-    c = hi
-    for k in range(3, -1, -1):
-        ck = min(lo + step * k, hi)
-        if sum(cdiv(int(x), ck) for x in lens) <= bound:
-            c = ck
-    big, small, f, parities = c + skew, c - skew, 0, []
-    for x in lens:
-        x = int(x)
-        q, rem = divmod(x, big + small)
-        first = big if f % 2 == 0 else small
-        parities.append(f % 2)
-        f += 2 * q + (0 if rem == 0 else (1 if rem <= first else 2))
-    return c, f, parities
-
-
 def test_split_many_rows_alternating_chunks():
     """130 split rows (three 64-row slots of the plan's scans) of 3000-9000
-    entries, where the alternating chunk sizes fit the bound: rows start on
-    even and odd chunks across the slots, so the parity carried between
-    slots decides every later row's chunks.  One row empty, one all masked,
-    10% of entries masked; all rows against the oracle."""
+    entries, where the alternating chunk sizes fit the bound (the plan's rule
+    restated in tests.helpers says so): rows start on even and odd chunks
+    across the slots, so the parity carried between slots decides every
+    later row's chunks.  One row empty, one all masked, 10% of entries
+    masked; all rows against the oracle."""
     t = 130
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     g = torch.Generator().manual_seed(61)
@@ -215,10 +189,12 @@ def test_split_many_rows_alternating_chunks():
     idx[ptr[100]:ptr[101]] = -1
     bound = mla.split_workgroups(t, idx.size, cus)
     assert bound > 0
-    c, total, parities = _alternating_chunk_total(lens, bound)
-    assert total <= bound, "the alternating sizes must fit for this test to reach them"
-    assert 0 < sum(parities[64:]) < t - 64, "later slots must hold rows starting on both parities"
-    say(f"split T={t}, bound {bound}: base chunk {c}, {total} alternating chunks")
+    big, small = plan_chunk_sizes(lens, bound)
+    first = plan_first_chunks(lens, big, small)
+    assert big > small, "the alternating sizes must fit for this test to reach them"
+    parities = [x % 2 for x in first[64:t]]
+    assert 0 < sum(parities) < t - 64, "later slots must hold rows starting on both parities"
+    say(f"split T={t}, bound {bound}: chunks of {big} / {small} entries, {first[-1]} in all")
     out, lse = run(q, rec, ptr, idx, torch.int32)
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
     assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t} alternating chunks")
