@@ -198,3 +198,30 @@ def test_split_many_rows_alternating_chunks():
     out, lse = run(q, rec, ptr, idx, torch.int32)
     ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
     assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t} alternating chunks")
+
+
+@pytest.mark.parametrize("t", [63, 64, 65, 127, 128, 129, 255, 256, 257, 511])
+def test_split_row_counts_across_plan_slots(t):
+    """Row counts on both sides of the plan's 64-row slots (lane l holds rows
+    l, l + 64, ...; a slot past the last row reads indptr[T]), up to the
+    split pass's 512-row limit, rows of 520-2600 entries, one empty: all
+    rows against the oracle, whichever chunk sizes the rule picks."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator().manual_seed(70 + t)
+    n = 4096
+    q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
+    kv_c = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    k_pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
+    lens = torch.randint(520, 2601, (t,), generator=g).numpy().astype(np.int64)
+    lens[t - 1 if t % 2 else t // 2] = 0
+    ptr = np.concatenate([[0], np.cumsum(lens)])
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g).numpy().astype(np.int64)
+    idx[torch.rand(int(ptr[-1]), generator=g).numpy() < 0.05] = -1
+    bound = mla.split_workgroups(t, idx.size, cus)
+    assert bound > 0
+    big, small = plan_chunk_sizes(lens, bound)
+    say(f"split T={t}, bound {bound}: chunks of {big} / {small} entries")
+    out, lse = run(q, rec, ptr, idx, torch.int32)
+    ref_out, ref_lse = oracle_fwd(bf16_bits(q), rec, ptr, idx, SCALE)
+    assert_fwd_close(out, lse, ref_out, ref_lse, f"split T={t} across plan slots")
