@@ -112,8 +112,9 @@ constexpr int64_t kMinChunkEntries = 512;
 // workgroup per row; otherwise the number of workgroups of the partial pass,
 // an upper bound on the chunks.  Split when the rows alone cannot give two
 // workgroups per compute unit and the average row is longer than a minimum
-// chunk; the plan kernel then sizes the chunks on the device so they fit
-// those 2 x CU workgroups in one round.  A forced chunk size (flags) gives
+// chunk, unless more than CU-many rows look equal (below); the plan kernel
+// then sizes the chunks on the device so they fit those 2 x CU workgroups
+// in one round.  A forced chunk size (flags) gives
 // the bound ceil(nnz / chunk) + T.
 int64_t plan_split(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags, int32_t *forced_chunk) {
   const uint32_t forced = (flags & MLA_FLAG_CHUNK_MASK) >> 16;
@@ -127,6 +128,11 @@ int64_t plan_split(int64_t tokens, int64_t nnz, int32_t cus, uint32_t flags, int
   const int64_t target = 2 * (int64_t)cus;
   if (tokens >= target || tokens > mla::kMaxSplitRows) return 0;
   if ((nnz + tokens - 1) / tokens <= kMinChunkEntries) return 0;
+  // Rows of equal length (an entry count that T divides, as a top-k
+  // selection gives) cannot be cut into two chunks each once 2T exceeds the
+  // workgroups: the split pass would compute what one workgroup per row
+  // does, plus a merge.
+  if (2 * tokens > target && nnz % tokens == 0) return 0;
   return target;
 }
 

@@ -81,7 +81,9 @@ typedef enum mla_status {
  *     lse[t,h]   = ln sum_j exp(z_j)           (float32, natural log).
  * A row with no such entry gives out = 0 and lse = -inf.  A slot listed
  * twice counts twice.  When there are too few rows to fill the GPU (and at
- * most 512), each row's entries are cut into chunks (split-KV): every
+ * most 512; above CU-many rows, not when T divides the entry count, rows of
+ * one length then having no room for two chunks each), each row's entries
+ * are cut into chunks (split-KV): every
  * workgroup of a partial pass plans the chunks from indptr on the device
  * and computes one chunk's float32 partial and LSE, and a second
  * launch combines each row's partials by their LSEs (the merge named by

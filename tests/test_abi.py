@@ -171,6 +171,9 @@ def test_insert_zero_tokens_is_a_no_op():
     (8, 8 * 131072, 256, 0, 512),       # long context: one round of 2 x CUs
     (64, 294912, 256, 0, 512),          # paged decode
     (8, 100, 256, 0, 0),
+    (300, 300 * 2048, 256, 0, 0),       # > CU-many equal rows: one chunk each at most, no split
+    (300, 300 * 2048 + 1, 256, 0, 512), # unequal rows: the plan balances them
+    (256, 256 * 2048, 256, 0, 512),     # CU-many equal rows: two chunks each
     (8, 8 * 131072, 256, 7, 2341 + 8),  # forced 7 tiles: ceil(nnz / 448) + T
     (4096, 100, 256, 1, 2 + 4096),      # forced even with many rows
     (0, 0, 256, 0, 0),

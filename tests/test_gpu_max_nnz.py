@@ -1,7 +1,8 @@
 """The forward at the index-count limit: just under 2^29 CSR entries (the
 most the C ABI accepts), int32 indices, once with one workgroup per row
 (4096 rows of 131,071 entries) and once through the split pass (511 rows of
-1,050,623 entries).  The entries are drawn on the device by torch's seeded
+1,050,623 entries, the last one entry shorter: rows of one length above
+CU-many rows take one workgroup each).  The entries are drawn on the device by torch's seeded
 generator over a 4096-record pool (5% masked); the oracle checks sampled
 rows from the same index values.  A 1M-entry row is too big for the oracle
 in one piece, so it is computed in 8 slices and the slices are combined by
@@ -25,7 +26,7 @@ MAX_INDICES = 1 << 29
 N = 4096
 
 
-def problem(t, per_row, seed):
+def problem(t, per_row, seed, short_last=False):
     assert t * per_row < MAX_INDICES
     g = torch.Generator().manual_seed(seed)
     q = torch.randn((t, 16, 576), generator=g).to(torch.bfloat16)
@@ -33,11 +34,13 @@ def problem(t, per_row, seed):
     k_pe = torch.randn((N, 64), generator=g).to(torch.bfloat16)
     rec = encode_records(bf16_bits(kv_c), bf16_bits(k_pe))
     gd = torch.Generator(device=DEV).manual_seed(seed)
-    idx = torch.randint(0, N, (t * per_row,), generator=gd, device=DEV, dtype=torch.int32)
-    mask = torch.rand((t * per_row,), generator=gd, device=DEV) < 0.05
+    nnz = t * per_row - (1 if short_last else 0)
+    idx = torch.randint(0, N, (nnz,), generator=gd, device=DEV, dtype=torch.int32)
+    mask = torch.rand((nnz,), generator=gd, device=DEV) < 0.05
     idx.masked_fill_(mask, -1)
     del mask
     ptr = torch.arange(t + 1, dtype=torch.int64) * per_row
+    ptr[-1] = nnz
     return q, rec, ptr, idx
 
 
@@ -59,7 +62,7 @@ def oracle_row(q, rec, idx_row, slices):
 ])
 def test_forward_at_the_index_limit(t, per_row, rows, slices):
     say(f"max nnz: T={t} x {per_row} = {t * per_row} entries")
-    q, rec, ptr, idx = problem(t, per_row, 60 + t)
+    q, rec, ptr, idx = problem(t, per_row, 60 + t, short_last=t < 512)
     split = mla.split_workgroups(t, idx.numel(), torch.cuda.get_device_properties(0).multi_processor_count)
     assert (split > 0) == (t < 512)
     out, lse = mla.sparse_fwd(q.to(DEV), torch.from_numpy(rec).to(DEV), ptr.to(torch.int32).to(DEV), idx,
@@ -67,7 +70,7 @@ def test_forward_at_the_index_limit(t, per_row, rows, slices):
     torch.cuda.synchronize()
     say("forward done; checking sampled rows")
     for r in rows:
-        idx_row = idx[r * per_row:(r + 1) * per_row].cpu().numpy().astype(np.int64)
+        idx_row = idx[int(ptr[r]):int(ptr[r + 1])].cpu().numpy().astype(np.int64)
         ref_out, ref_lse = oracle_row(q[r], rec, idx_row, slices)
         assert_fwd_close(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, f"row {r}")
         say(f"row {r} ok")
