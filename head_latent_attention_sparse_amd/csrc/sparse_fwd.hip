@@ -89,6 +89,7 @@ struct FwdKernelArgs {
   int64_t ennz;
   const float *sink;  // [heads] sink logits (natural-log units of the scaled logits), or nullptr
   int64_t guess_len;  // one workgroup per row: rows most likely start at t * guess_len (0: no guess)
+  int32_t direct_single;  // split pass: a row of one chunk writes out / lse itself (the merge skips it)
 };
 
 // A workgroup's share of a row.  Entry v of the row (0 <= v < lenp + lene)
@@ -97,6 +98,7 @@ struct FwdKernelArgs {
 struct RowRange {
   int64_t t, beg, lenp, ebeg, vb, ve;
   int64_t chunk;  // split pass: the chunk's index in row order (its partial's slot)
+  bool single;    // split pass: the chunk is its row's only one
 };
 
 // Clamp a CSR pair to [0, nnz] (a decreasing pair gives an empty range).
@@ -358,6 +360,7 @@ __device__ bool split_plan(const FwdKernelArgs &p, RowRange &rr) {
       rr.lenp = __builtin_amdgcn_readlane(lp[j], src);
       rr.ebeg = __builtin_amdgcn_readlane(eb[j], src);
       rr.chunk = jc;
+      rr.single = __builtin_amdgcn_readlane(kr, src) == 1;
       found = true;
     }
     carry += __builtin_amdgcn_readlane((carry & 1) ? S1[j] : S0[j], 63);
@@ -722,6 +725,19 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_fwd_kernel(FwdKernelArgs p
       }
       if (kLse && wave == 0 && g == 0)
         p.lse[t * p.heads + n] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
+    } else if (p.direct_single && rr.single) {
+      // The row's only chunk: out and lse as the merge would make them of this
+      // one partial (bit for bit: a single partial o merges to o * 1, its LSE
+      // to lse + log2 1), so the merge skips the row.
+      uint16_t *orow = p.out + t * p.o_st + (int64_t)n * p.o_sh + 128 * wave + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t *dst = reinterpret_cast<uint32_t *>(orow + 16 * m);
+        dst[0] = pack_bf16x2(oacc[m][0] * inv, oacc[m][1] * inv);
+        dst[1] = pack_bf16x2(oacc[m][2] * inv, oacc[m][3] * inv);
+      }
+      if (p.lse && wave == 0 && g == 0)
+        p.lse[t * p.heads + n] = empty ? -INFINITY : (m_run + fast_log2(l_tot)) * kLn2;
     } else {
       const int64_t row = rr.chunk * p.heads + n;  // chunk index * H + head
       float *wo = p.ws_out + row * kLatent + 128 * wave + 4 * g;
@@ -749,7 +765,7 @@ template <bool kLse, int kLanes>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_out, const float *ws_lse,
                                                               const int32_t *prefix, int32_t heads, uint16_t *out,
                                                               int64_t o_st, int64_t o_sh, float *lse,
-                                                              const float *sink) {
+                                                              const float *sink, int32_t direct_single) {
   constexpr int kQuads = kMergeThreads / kLanes;
   constexpr int kParts = kLatent / (4 * kQuads);
   __shared__ MergeAcc s_acc[kLanes][kQuads];
@@ -760,6 +776,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *ws_ou
   const int h = (int)(th - t * heads);
   const int64_t c0 = prefix[t];
   const int nc = prefix[t + 1] - (int)c0;
+  if (direct_single && nc == 1) return;  // the partial pass wrote this row (whole workgroup)
   const float *lp = ws_lse + c0 * heads + h;  // chunk s at lp[s * heads]
   const int cl = tid / kQuads;  // chunk lane
   const int cq = tid % kQuads;  // column quad
@@ -802,10 +819,12 @@ void launch_merge(const FwdArgs &a, hipStream_t stream) {
   const dim3 mgrid((unsigned)((int64_t)a.num_tokens * a.num_heads * (kLanes / 2)));
   if (a.lse)
     merge_kernel<true, kLanes><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                                    a.out_stride_token, a.out_stride_head, a.lse, a.sink);
+                                                                    a.out_stride_token, a.out_stride_head, a.lse, a.sink,
+                                                                    a.vp_w == nullptr && a.sink == nullptr);
   else
     merge_kernel<false, kLanes><<<mgrid, kMergeThreads, 0, stream>>>(a.ws_out, a.ws_lse, a.ws_prefix, a.num_heads, a.out,
-                                                                     a.out_stride_token, a.out_stride_head, nullptr, a.sink);
+                                                                     a.out_stride_token, a.out_stride_head, nullptr, a.sink,
+                                                                     a.vp_w == nullptr && a.sink == nullptr);
 }
 
 template <typename IdxT, bool kExtra>
@@ -838,6 +857,9 @@ hipError_t launch_typed(const FwdArgs &a, hipStream_t stream) {
   k.ennz = a.extra_num_indices;
   k.sink = a.sink;
   k.guess_len = a.row_len_guess;
+  // a row of one chunk is written by the partial pass unless a sink joins it
+  // in the merge or the fused projection merges it
+  k.direct_single = a.vp_w == nullptr && a.sink == nullptr;
   const dim3 block(kThreads);
   const bool lse = a.lse != nullptr;
   if (a.chunk_bound <= 0) {
