@@ -153,3 +153,35 @@ def test_fused_zero_tokens_and_rejections():
         mla.sparse_fwd_v_up_proj(q, pool, ptr, idx, SCALE, w[:8])  # weights for another head count
     with pytest.raises(ValueError):
         mla.sparse_fwd_v_up_proj(q, pool, ptr, idx, SCALE, wp, gate=gate[:, :100])
+
+
+@pytest.mark.parametrize("return_lse", [True, False])
+def test_single_chunk_rows_written_directly_equal_the_merge(return_lse):
+    """With forced 2-tile chunks, rows of at most 128 entries have one chunk:
+    the plain forward writes their out / lse from the partial pass (the merge
+    skips them) while the fused call merges them; the two must agree bit for
+    bit on every row, one-chunk rows (some empty, some all masked) mixed with
+    rows of several chunks."""
+    say(f"one-chunk rows written directly (return_lse={return_lse})")
+    g = torch.Generator().manual_seed(31)
+    t, heads, n = 40, 16, 3000
+    q = torch.randn((t, heads, 576), generator=g).to(torch.bfloat16).to(DEV)
+    kv = torch.randn((n, 512), generator=g).to(torch.bfloat16)
+    pe = torch.randn((n, 64), generator=g).to(torch.bfloat16)
+    pool = torch.from_numpy(encode_records(bf16_bits(kv), bf16_bits(pe))).to(DEV)
+    lens = torch.tensor([[0, 1, 64, 100, 128][i % 5] if i % 2 == 0 else 129 + 97 * i for i in range(t)])
+    ptr = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lens, 0)]).to(torch.int32)
+    idx = torch.randint(0, n, (int(ptr[-1]),), generator=g, dtype=torch.int32)
+    idx[torch.rand(idx.shape, generator=g) < 0.1] = -1
+    idx[int(ptr[6]):int(ptr[7])] = -1  # a one-chunk row with every entry masked
+    w = (torch.randn((heads, 512, 128), generator=g) * 512 ** -0.5).to(torch.bfloat16).to(DEV)
+    wp = mla.prepare_w_uv(w)
+    ptr, idx = ptr.to(DEV), idx.to(DEV)
+    plain = mla.sparse_fwd(q, pool, ptr, idx, SCALE, has_invalid=True, return_lse=return_lse, chunk_tiles=2)
+    _, out_f, lse_f = mla.sparse_fwd_v_up_proj(q, pool, ptr, idx, SCALE, wp, has_invalid=True,
+                                               return_lse=return_lse, chunk_tiles=2)
+    torch.cuda.synchronize()
+    assert torch.equal(plain[0].view(torch.int16), out_f.view(torch.int16)), "out differs"
+    if return_lse:
+        assert torch.equal(plain[1].view(torch.int32), lse_f.view(torch.int32)), "lse differs"
+        assert torch.isneginf(plain[1][0]).all() and torch.isneginf(plain[1][6]).all()
