@@ -830,7 +830,7 @@ def _cpu_worker_rows(rows):
 class CpuOracle:
     """The fp64 numpy oracle forward over all rows of a workload, in blocks of
     rows on a pool of worker processes (one per core the process may use, at
-    most 16: a GPU machine's CPU share)."""
+    most 16, the host cores that one GPU of the machine is given)."""
 
     def __init__(self, w, seg=None, workers=0):
         import multiprocessing

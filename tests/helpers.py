@@ -38,7 +38,7 @@ def oracle_encode(kv_c, k_pe):
 
 def oracle_threads():
     """Threads for oracle work: the CPUs this process may use, at most 16
-    (a GPU machine's CPU share).  numpy releases the GIL in the oracle's array
+    (the host cores that one GPU of the machine is given).  numpy releases the GIL in the oracle's array
     work, so threads share it without extra processes."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
