@@ -23,7 +23,7 @@ FILL = 0x5A
 
 def run_both(ql, qp, kv, kp, slots, n_rec, positions=None, table=None, mqa_q=None):
     """The GPU epilogue and the oracle on the same inputs; returns
-    (gpu mqa bits, gpu pool, oracle mqa bits, oracle pool)."""
+    (device mqa bits, device pool, oracle mqa bits, oracle pool)."""
     pool = torch.full((n_rec, 656), FILL, dtype=torch.uint8, device=DEV)
     out = mla.decode_q_concat_insert(
         ql.to(DEV), qp.to(DEV), kv.to(DEV), kp.to(DEV), pool, slots.to(DEV),

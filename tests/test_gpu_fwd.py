@@ -2,7 +2,7 @@
 
 Bar (the tolerance of the hot-path statement): |out - ref| <= 1e-2 + 1e-2 |ref| elementwise,
 |lse - ref| <= 2e-3, -inf exactly where the oracle has an empty row.  The
-GPU pools are built by mla_cache_insert and first checked byte for byte
+Device pools are built by mla_cache_insert and first checked byte for byte
 against the oracle's writer; the oracle works from its own records.
 """
 
@@ -47,7 +47,7 @@ def check_rows(w, pool, out, lse, rows, what):
     needed = np.concatenate([indices[indptr[t]:indptr[t + 1]] for t in rows]) if len(rows) else np.zeros(0)
     batches = w.setup_inserts + w.step_inserts
     uniq, sub = oracle_subpool(w.num_records, batches, needed)
-    # the GPU pool holds the oracle's bytes for these slots
+    # the device pool holds the oracle's bytes for these slots
     got = pool[torch.from_numpy(uniq).to(DEV)].cpu().numpy() if uniq.size else sub
     assert np.array_equal(got, sub), f"{what}: inserted records differ from the oracle writer"
     ptr, ind = remap_rows(indptr, indices, rows, uniq, w.num_records)
@@ -112,7 +112,7 @@ def check_full_workload(w, what):
     """Every row of a full-size workload against the oracle, in the launch
     configuration bench.py times (the binding with a caller workspace).  The
     oracle's pool comes from its own writer applied to the workload's insert
-    batches; the GPU pool (built by mla_cache_insert) must equal it byte for
+    batches; the device pool (built by mla_cache_insert) must equal it byte for
     byte first.  Then the properties that hold at any size."""
     pool, view = build_gpu_pool(w)
     ref_pool = oracle_pool(w.num_records, w.setup_inserts + w.step_inserts)

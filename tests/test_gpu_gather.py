@@ -18,7 +18,7 @@ DEV = "cuda:0"
 
 
 def build(w):
-    """GPU pool [nb, bs, 656] and the oracle's pool; checks they are equal."""
+    """device pool [nb, bs, 656] and the oracle's pool; checks they are equal."""
     pool = torch.zeros((w.num_records // w.block_size, w.block_size, 656), dtype=torch.uint8, device=DEV)
     for b in w.setup_inserts:
         mla.cache_insert(b.kv_c.to(DEV), b.k_pe.to(DEV), b.slots.to(DEV), pool)
